@@ -1,0 +1,446 @@
+// C ABI of libmoe: validation, workspace layout and kernel launches.
+// The operations and their readings are documented in include/moe.h.
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "moe.h"
+#include "gemm.h"
+#include "moe_common.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, where)                    \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+struct Q {  // validated, derived dimensions
+  int64_t T, D, L, E, k, R, X, W, WX, H, S, HS, esize, scap, rcap, prow, row_bytes, my_rank;
+  bool bf16;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int derive(const moe_dims* d, Q* q) {
+  if (!d) return fail(MOE_EINVAL, "dims is NULL");
+  if (d->act_dtype != MOE_ACT_BF16 && d->act_dtype != MOE_ACT_F32)
+    return fail(MOE_EDTYPE, "act_dtype %d is not MOE_ACT_BF16 (0) or MOE_ACT_F32 (1)", d->act_dtype);
+  if (d->tokens < 0 || d->d_model <= 0 || d->latent <= 0 || d->n_experts <= 0 || d->top_k <= 0 ||
+      d->n_ranks <= 0 || d->waves <= 0 || d->expert_hidden <= 0 || d->shared_experts < 0 ||
+      d->shared_hidden <= 0)
+    return fail(MOE_EINVAL, "dims must be positive (tokens and shared_experts may be 0)");
+  if (d->n_experts % d->n_ranks) return fail(MOE_EINVAL, "n_experts %% n_ranks != 0");
+  const int X = d->n_experts / d->n_ranks;
+  if (X > MOE_MAX_LOCAL) return fail(MOE_EINVAL, "more than %d local experts", MOE_MAX_LOCAL);
+  if (X % d->waves) return fail(MOE_EINVAL, "local experts (%d) not divisible by waves (%d)", X, d->waves);
+  if (d->n_ranks > MOE_MAX_RANKS) return fail(MOE_EINVAL, "more than %d ranks", MOE_MAX_RANKS);
+  if (d->top_k > 32 || d->top_k > d->n_experts) return fail(MOE_EINVAL, "top_k must be <= min(32, n_experts)");
+  if (d->n_experts > 2048) return fail(MOE_EINVAL, "n_experts > 2048");
+  if (d->my_rank < 0 || d->my_rank >= d->n_ranks) return fail(MOE_EINVAL, "my_rank out of range");
+  if (d->send_num <= 0 || d->send_den <= 0 || d->recv_num <= 0 || d->recv_den <= 0)
+    return fail(MOE_EINVAL, "capacity factors must be positive rationals");
+  const bool bf16 = d->act_dtype == MOE_ACT_BF16;
+  if (bf16) {
+    if (d->d_model % 64 || d->latent % 64 || d->expert_hidden % 64 || d->shared_hidden % 64)
+      return fail(MOE_EINVAL, "bf16 layers need d_model, latent, expert_hidden, shared_hidden multiples of 64");
+  } else if (d->latent % 8) {
+    return fail(MOE_EINVAL, "fp32 layers need latent to be a multiple of 8");
+  }
+  q->T = d->tokens; q->D = d->d_model; q->L = d->latent; q->E = d->n_experts; q->k = d->top_k;
+  q->R = d->n_ranks; q->X = X; q->W = d->waves; q->WX = X / d->waves; q->H = d->expert_hidden;
+  q->S = d->shared_experts; q->HS = d->shared_hidden; q->my_rank = d->my_rank; q->bf16 = bf16;
+  q->esize = bf16 ? 2 : 4;
+  const int64_t assign = q->T * q->k;
+  q->scap = ceil_div((int64_t)d->send_num * assign, (int64_t)d->send_den * q->R);
+  q->rcap = ceil_div((int64_t)d->recv_num * q->R * assign, (int64_t)d->recv_den * q->E);
+  q->row_bytes = q->L * q->esize;
+  q->prow = ceil_div(q->row_bytes + 4, 128) * 128;
+  if (assign > (1ll << 30) || q->R * q->scap > (1ll << 30) || q->WX * q->rcap > (1ll << 30) ||
+      q->T * q->E > (1ll << 31) || q->T * q->D > (1ll << 40))
+    return fail(MOE_EINVAL, "sizes exceed the 32-bit index range of the kernels");
+  return MOE_OK;
+}
+
+struct WsLayout {
+  size_t ctr, s_cc, s_cb, s_lr, r_cc, r_cb, r_j, r_lr, r_rank, logits, h, cat, total;
+  int nch_s, nch_r;
+};
+
+WsLayout layout(const Q& q) {
+  WsLayout w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  w.nch_s = (int)ceil_div(q.T * q.k, SCAN_CHUNK);
+  w.nch_r = (int)ceil_div(q.R * q.scap, SCAN_CHUNK);
+  w.ctr = take((Ctr::HEADER + 2 * q.R + 2 * q.X) * 4);
+  w.s_cc = take((size_t)(q.R + 1) * w.nch_s * 4);
+  w.s_cb = take((size_t)(q.R + 1) * w.nch_s * 4);
+  w.s_lr = take((size_t)q.T * q.k * 4);
+  w.r_cc = take((size_t)(q.X + 1) * w.nch_r * 4);
+  w.r_cb = take((size_t)(q.X + 1) * w.nch_r * 4);
+  w.r_j = take((size_t)q.R * q.scap * 4);
+  w.r_lr = take((size_t)q.R * q.scap * 4);
+  w.r_rank = take((size_t)q.R * q.scap * 4);
+  w.logits = take((size_t)q.T * q.E * 4);
+  w.h = take((size_t)q.WX * q.rcap * q.H * q.esize);
+  w.cat = take((size_t)q.T * (q.L + q.S * q.HS) * q.esize);
+  w.total = off;
+  return w;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+#define NEED(p, name)                                                     \
+  do {                                                                    \
+    if (!(p)) return fail(MOE_EINVAL, "%s is NULL", name);                \
+    if (!aligned16(p)) return fail(MOE_EALIGN, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+// Index, weight and count arrays are read as 4-byte scalars.
+#define NEED4(p, name)                                                    \
+  do {                                                                    \
+    if (!(p)) return fail(MOE_EINVAL, "%s is NULL", name);                \
+    if ((uintptr_t)(p) & 3) return fail(MOE_EALIGN, "%s is not 4-byte aligned", name); \
+  } while (0)
+
+// A buffer of zero elements may be NULL.
+#define NEED_IF(cond, p, name) \
+  do {                         \
+    if (cond) NEED(p, name);   \
+  } while (0)
+#define NEED4_IF(cond, p, name) \
+  do {                          \
+    if (cond) NEED4(p, name);   \
+  } while (0)
+
+template <class P>
+P* at(void* ws, size_t off) { return (P*)((char*)ws + off); }
+
+// ---------------------------------------------------------------- GEMM runners
+
+template <bool GATEUP, class A, class B, class E>
+hipError_t gemm_bf16(A a, B b, E e, int N, int K, int64_t max_rows, int groups, hipStream_t st) {
+  constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
+  using TL = MfmaTile<BM, BN, WM, WN>;
+  if (N <= 0 || max_rows <= 0 || groups <= 0) return hipSuccess;
+  auto kern = gemm_bf16_mfma<BM, BN, WM, WN, GATEUP, A, B, E>;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t r = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::LDS_BYTES);
+    if (r != hipSuccess) return r;
+    attr = true;
+  }
+  const dim3 grid((unsigned)ceil_div(N, BN), (unsigned)ceil_div(max_rows, BM), (unsigned)groups);
+  hipLaunchKernelGGL(kern, grid, dim3(TL::NT), TL::LDS_BYTES, st, a, b, e, N, K);
+  return hipGetLastError();
+}
+
+template <bool GATEUP, class A, class B, class E>
+hipError_t gemm_f32(A a, B b, E e, int N, int K, int64_t max_rows, int groups, hipStream_t st) {
+  const int cols = GATEUP ? N / 2 : N;
+  if (cols <= 0 || max_rows <= 0 || groups <= 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(cols, 16), (unsigned)ceil_div(max_rows, 16), (unsigned)groups);
+  hipLaunchKernelGGL((gemm_f32_simple<GATEUP, A, B, E>), grid, dim3(16, 16), 0, st, a, b, e, N, K);
+  return hipGetLastError();
+}
+
+// route GEMM: logits | z = x . [W_r ; W_d]^T
+template <class T>
+hipError_t route_gemm(const Q& q, const void* x, const void* wr, const void* wd, const float* bias, int brt,
+                      float* logits, void* z, hipStream_t st) {
+  ARows<T> a{(const T*)x, q.D, 0, nullptr, (int)q.T};
+  BTwo<T> b{(const T*)wr, (const T*)wd, (int)q.E, q.D};
+  ERouteDown<T> e{logits, (T*)z, bias, (int)q.E, (int)q.L, brt};
+  if constexpr (sizeof(T) == 2) return gemm_bf16<false>(a, b, e, (int)(q.E + q.L), (int)q.D, q.T, 1, st);
+  else return gemm_f32<false>(a, b, e, (int)(q.E + q.L), (int)q.D, q.T, 1, st);
+}
+
+template <class T, class A>
+hipError_t expert_gemms(const Q& q, A a1, int wave, const int32_t* row_src, const int32_t* wave_count,
+                        const void* w13, const void* w2, void* ret, int64_t ret_src_stride, T* h, hipStream_t st) {
+  const int64_t x0 = (int64_t)wave * q.WX;
+  BGateUp<T> b1{(const T*)w13 + x0 * 2 * q.H * q.L, q.L, 2 * q.H * q.L, (int)q.H, 0};
+  ESwiGLU<T> e1{h, q.H, q.rcap * q.H, 0};
+  ARows<T> a2{h, q.H, q.rcap * q.H, wave_count, 0};
+  BRows<T> b2{(const T*)w2 + x0 * q.L * q.H, q.H, q.L * q.H};
+  EScatter<T> e2{(char*)ret, ret_src_stride, q.row_bytes, (int)q.scap, row_src, q.rcap};
+  hipError_t r;
+  if constexpr (sizeof(T) == 2) {
+    r = gemm_bf16<true>(a1, b1, e1, (int)(2 * q.H), (int)q.L, q.rcap, (int)q.WX, st);
+    if (r != hipSuccess) return r;
+    return gemm_bf16<false>(a2, b2, e2, (int)q.L, (int)q.H, q.rcap, (int)q.WX, st);
+  } else {
+    r = gemm_f32<true>(a1, b1, e1, (int)(2 * q.H), (int)q.L, q.rcap, (int)q.WX, st);
+    if (r != hipSuccess) return r;
+    return gemm_f32<false>(a2, b2, e2, (int)q.L, (int)q.H, q.rcap, (int)q.WX, st);
+  }
+}
+
+template <class T>
+hipError_t shared_and_up(const Q& q, const void* x, const void* ws13, const void* ws2, const void* w_up, T* cat,
+                         void* out, hipStream_t st) {
+  const int64_t ldc = q.L + q.S * q.HS;
+  ARows<T> a1{(const T*)x, q.D, 0, nullptr, (int)q.T};
+  BGateUp<T> b1{(const T*)ws13, q.D, 0, (int)q.HS, 2 * q.HS * q.D};
+  ESwiGLU<T> e1{cat, ldc, 0, (int)q.L};
+  ARows<T> a2{cat, ldc, 0, nullptr, (int)q.T};
+  BKSeg<T> b2{(const T*)w_up, q.L, (int)q.L, (const T*)ws2, q.HS, (int)q.HS, q.D * q.HS};
+  EStore<T> e2{(T*)out, q.D};
+  hipError_t r;
+  if constexpr (sizeof(T) == 2) {
+    if (q.S > 0) {
+      r = gemm_bf16<true>(a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
+      if (r != hipSuccess) return r;
+    }
+    return gemm_bf16<false>(a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
+  } else {
+    if (q.S > 0) {
+      r = gemm_f32<true>(a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
+      if (r != hipSuccess) return r;
+    }
+    return gemm_f32<false>(a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
+  }
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_capacity(const moe_dims* dims, int64_t* send_cap, int64_t* recv_cap, int64_t* pool_stride_bytes) {
+  Q q;
+  const int rc = derive(dims, &q);
+  if (rc) return rc;
+  if (send_cap) *send_cap = q.scap;
+  if (recv_cap) *recv_cap = q.rcap;
+  if (pool_stride_bytes) *pool_stride_bytes = q.prow;
+  return MOE_OK;
+}
+
+int moe_workspace_size(const moe_dims* dims, size_t* bytes) {
+  Q q;
+  const int rc = derive(dims, &q);
+  if (rc) return rc;
+  if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+  *bytes = layout(q).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_dims* dims, const void* x, const void* w_router, const void* w_down, const float* bias,
+              int32_t bias_row_tokens, float* logits, void* z, int32_t* topk_idx, float* topk_w, void* ws,
+              void* stream) {
+  Q q;
+  int rc = derive(dims, &q);
+  if (rc) return rc;
+  if (q.T == 0) return MOE_OK;
+  NEED(x, "x"); NEED(w_router, "w_router"); NEED(w_down, "w_down"); NEED(z, "z");
+  NEED4(topk_idx, "topk_idx"); NEED4(topk_w, "topk_w"); NEED(ws, "ws");
+  if (logits && ((uintptr_t)logits & 3)) return fail(MOE_EALIGN, "logits is not 4-byte aligned");
+  if (bias_row_tokens < 0) return fail(MOE_EINVAL, "bias_row_tokens < 0");
+  const WsLayout w = layout(q);
+  hipStream_t st = (hipStream_t)stream;
+  float* lg = logits ? logits : at<float>(ws, w.logits);
+  HIP_TRY(q.bf16 ? route_gemm<bf16_t>(q, x, w_router, w_down, bias, bias_row_tokens, lg, z, st)
+                 : route_gemm<float>(q, x, w_router, w_down, bias, bias_row_tokens, lg, z, st),
+          "moe_route gemm");
+  HIP_TRY(launch_select_topk(lg, (int)q.T, (int)q.E, (int)q.k, topk_idx, topk_w, st), "moe_route select");
+  return MOE_OK;
+}
+
+int moe_pack_pools(const moe_dims* dims, const void* z, const int32_t* topk_idx, void* send_pools,
+                   int64_t dst_stride_bytes, int32_t* slot_of, int32_t* send_count, void* ws, void* stream) {
+  Q q;
+  int rc = derive(dims, &q);
+  if (rc) return rc;
+  NEED_IF(q.scap > 0, send_pools, "send_pools"); NEED4(send_count, "send_count"); NEED(ws, "ws");
+  if (q.T > 0) { NEED(z, "z"); NEED4(topk_idx, "topk_idx"); NEED4(slot_of, "slot_of"); }
+  if (dst_stride_bytes % 16 || dst_stride_bytes < q.scap * q.prow)
+    return fail(MOE_EALIGN, "dst_stride_bytes must be a multiple of 16 and >= send_cap * pool_stride_bytes");
+  const WsLayout w = layout(q);
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* ctr = at<int32_t>(ws, w.ctr);
+  HIP_TRY(launch_send_rank(topk_idx, (int)(q.T * q.k), (int)q.X, (int)q.E, (int)q.R, at<int32_t>(ws, w.s_lr),
+                           at<int32_t>(ws, w.s_cc), st), "moe_pack_pools rank");
+  HIP_TRY(launch_send_scan(at<int32_t>(ws, w.s_cc), w.nch_s, (int)q.R, (int)q.scap, at<int32_t>(ws, w.s_cb), ctr,
+                           send_count, st), "moe_pack_pools scan");
+  HIP_TRY(launch_pack(z, q.row_bytes, topk_idx, at<int32_t>(ws, w.s_lr), at<int32_t>(ws, w.s_cb), (int)q.T,
+                      (int)q.k, (int)q.X, (int)q.E, (int)q.R, (int)q.scap, send_pools, dst_stride_bytes, q.prow,
+                      slot_of, send_count, st), "moe_pack_pools pack");
+  return MOE_OK;
+}
+
+int moe_recv_waves(const moe_dims* dims, const void* recv_pools, int64_t src_stride_bytes, int32_t wave,
+                   void* wave_buf, int32_t* row_src, int32_t* wave_count, void* ws, void* stream) {
+  Q q;
+  int rc = derive(dims, &q);
+  if (rc) return rc;
+  NEED_IF(q.scap > 0, recv_pools, "recv_pools"); NEED4_IF(q.rcap > 0, row_src, "row_src");
+  NEED4(wave_count, "wave_count"); NEED(ws, "ws");
+  if (wave_buf && !aligned16(wave_buf)) return fail(MOE_EALIGN, "wave_buf is not 16-byte aligned");
+  if (wave < 0 || wave >= q.W) return fail(MOE_EINVAL, "wave %d out of range [0, %d)", wave, (int)q.W);
+  if (src_stride_bytes % 16 || src_stride_bytes < q.scap * q.prow)
+    return fail(MOE_EALIGN, "src_stride_bytes must be a multiple of 16 and >= send_cap * pool_stride_bytes");
+  const WsLayout w = layout(q);
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* ctr = at<int32_t>(ws, w.ctr);
+  const int j0 = wave * (int)q.WX, nj = (int)q.WX, n_rows = (int)(q.R * q.scap);
+  int32_t* arrivals = ctr + Ctr::HEADER + 2 * q.R;
+  int32_t* kept = arrivals + q.X;
+  HIP_TRY(launch_recv_rank(recv_pools, src_stride_bytes, q.prow, q.row_bytes, (int)q.R, (int)q.scap, (int)q.X,
+                           (int)q.my_rank, at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cc),
+                           st), "moe_recv_waves rank");
+  HIP_TRY(launch_recv_scan(at<int32_t>(ws, w.r_cc), w.nch_r, (int)q.X, (int)q.rcap, j0, nj, at<int32_t>(ws, w.r_cb),
+                           arrivals, kept, ctr + Ctr::RECV_BAD, wave_count, st), "moe_recv_waves scan");
+  HIP_TRY(launch_recv_place(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cb), n_rows,
+                            (int)q.X, (int)q.rcap, j0, nj, wave_count, at<int32_t>(ws, w.r_rank), row_src, st),
+          "moe_recv_waves place");
+  if (wave_buf)
+    HIP_TRY(launch_wave_gather(recv_pools, src_stride_bytes, q.prow, (int)q.scap, q.row_bytes, row_src, wave_count,
+                               nj, (int)q.rcap, wave_buf, st), "moe_recv_waves gather");
+  return MOE_OK;
+}
+
+int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf, const void* recv_pools,
+                    int64_t src_stride_bytes, const int32_t* row_src, const int32_t* wave_count, const void* w13,
+                    const void* w2, void* ret_pools, int64_t ret_src_stride_bytes, void* ws, void* stream) {
+  Q q;
+  int rc = derive(dims, &q);
+  if (rc) return rc;
+  NEED4_IF(q.rcap > 0, row_src, "row_src"); NEED4(wave_count, "wave_count"); NEED(w13, "w13"); NEED(w2, "w2");
+  NEED_IF(q.scap > 0, ret_pools, "ret_pools"); NEED(ws, "ws");
+  if (wave < 0 || wave >= q.W) return fail(MOE_EINVAL, "wave %d out of range [0, %d)", wave, (int)q.W);
+  if (ret_src_stride_bytes % 16 || ret_src_stride_bytes < q.scap * q.row_bytes)
+    return fail(MOE_EALIGN, "ret_src_stride_bytes must be a multiple of 16 and >= send_cap * L * sizeof(act)");
+  if (wave_buf) {
+    if (!aligned16(wave_buf)) return fail(MOE_EALIGN, "wave_buf is not 16-byte aligned");
+  } else {
+    NEED_IF(q.scap > 0, recv_pools, "recv_pools (wave_buf is NULL)");
+    if (src_stride_bytes % 16 || src_stride_bytes < q.scap * q.prow)
+      return fail(MOE_EALIGN, "src_stride_bytes must be a multiple of 16 and >= send_cap * pool_stride_bytes");
+  }
+  const WsLayout w = layout(q);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t r;
+  if (q.bf16) {
+    bf16_t* h = at<bf16_t>(ws, w.h);
+    if (wave_buf) {
+      ARows<bf16_t> a{(const bf16_t*)wave_buf, q.L, q.rcap * q.L, wave_count, 0};
+      r = expert_gemms<bf16_t>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, st);
+    } else {
+      AGather<bf16_t> a{(const char*)recv_pools, src_stride_bytes, q.prow, (int)q.scap, row_src, q.rcap, wave_count};
+      r = expert_gemms<bf16_t>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, st);
+    }
+  } else {
+    float* h = at<float>(ws, w.h);
+    if (wave_buf) {
+      ARows<float> a{(const float*)wave_buf, q.L, q.rcap * q.L, wave_count, 0};
+      r = expert_gemms<float>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, st);
+    } else {
+      AGather<float> a{(const char*)recv_pools, src_stride_bytes, q.prow, (int)q.scap, row_src, q.rcap, wave_count};
+      r = expert_gemms<float>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, st);
+    }
+  }
+  HIP_TRY(r, "moe_expert_gemm gemm");
+  HIP_TRY(launch_zero_dropped(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_rank), (int)(q.R * q.scap), (int)q.scap,
+                              (int)q.rcap, wave * (int)q.WX, (int)q.WX, ret_pools, ret_src_stride_bytes, q.row_bytes,
+                              st), "moe_expert_gemm zero rows");
+  return MOE_OK;
+}
+
+int moe_combine(const moe_dims* dims, const void* ret_pools, int64_t ret_dst_stride_bytes, const int32_t* slot_of,
+                const float* topk_w, const void* w_up, const void* x, const void* ws13, const void* ws2, void* out,
+                void* ws, void* stream) {
+  Q q;
+  int rc = derive(dims, &q);
+  if (rc) return rc;
+  if (q.T == 0) return MOE_OK;
+  NEED(ret_pools, "ret_pools"); NEED(w_up, "w_up"); NEED(out, "out"); NEED(ws, "ws");
+  NEED4(slot_of, "slot_of"); NEED4(topk_w, "topk_w"); NEED(x, "x");
+  if (q.S > 0) { NEED(ws13, "ws13"); NEED(ws2, "ws2"); }
+  if (ret_dst_stride_bytes % 16 || ret_dst_stride_bytes < q.scap * q.row_bytes)
+    return fail(MOE_EALIGN, "ret_dst_stride_bytes must be a multiple of 16 and >= send_cap * L * sizeof(act)");
+  const WsLayout w = layout(q);
+  hipStream_t st = (hipStream_t)stream;
+  void* cat = at<char>(ws, w.cat);
+  const int64_t ldc = q.L + q.S * q.HS;
+  HIP_TRY(launch_combine(q.bf16 ? 0 : 1, ret_pools, ret_dst_stride_bytes, q.row_bytes, (int)q.scap, slot_of, topk_w,
+                         (int)q.T, (int)q.k, (int)q.L, cat, ldc, st), "moe_combine combine");
+  HIP_TRY(q.bf16 ? shared_and_up<bf16_t>(q, x, ws13, ws2, w_up, (bf16_t*)cat, out, st)
+                 : shared_and_up<float>(q, x, ws13, ws2, w_up, (float*)cat, out, st),
+          "moe_combine gemm");
+  return MOE_OK;
+}
+
+int moe_drop_stats(const moe_dims* dims, const void* ws, moe_drop_report* rep, void* stream) {
+  Q q;
+  int rc = derive(dims, &q);
+  if (rc) return rc;
+  NEED(ws, "ws");
+  if (!rep) return fail(MOE_EINVAL, "report is NULL");
+  const WsLayout w = layout(q);
+  const size_t n = Ctr::HEADER + 2 * q.R + 2 * q.X;
+  std::string buf(n * 4, '\0');
+  int32_t* c = (int32_t*)&buf[0];
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipMemcpyAsync(c, (const char*)ws + w.ctr, n * 4, hipMemcpyDeviceToHost, st), "moe_drop_stats copy");
+  HIP_TRY(hipStreamSynchronize(st), "moe_drop_stats sync");
+  *rep = moe_drop_report{};
+  rep->n_ranks = (int32_t)q.R;
+  rep->local_experts = (int32_t)q.X;
+  rep->send_assignments = q.T * q.k;
+  int64_t kept = 0, dropped = c[Ctr::SEND_INVALID];
+  for (int d = 0; d < q.R; ++d) {
+    rep->send_demand[d] = c[Ctr::HEADER + d];
+    rep->send_count[d] = c[Ctr::HEADER + q.R + d];
+    kept += rep->send_count[d];
+    dropped += rep->send_demand[d] - rep->send_count[d];
+  }
+  rep->send_kept = kept;
+  rep->send_dropped = dropped;
+  int64_t arr = 0, kp = 0;
+  for (int j = 0; j < q.X; ++j) {
+    rep->expert_arrivals[j] = c[Ctr::HEADER + 2 * q.R + j];
+    rep->expert_kept[j] = c[Ctr::HEADER + 2 * q.R + q.X + j];
+    arr += rep->expert_arrivals[j];
+    kp += rep->expert_kept[j];
+  }
+  rep->recv_arrivals = arr;
+  rep->recv_kept = kp;
+  rep->recv_dropped = arr - kp;
+  rep->recv_bad_ids = c[Ctr::RECV_BAD];
+  if (rep->recv_bad_ids) return fail(MOE_ECAP, "%lld received rows carry an expert id of another rank",
+                                     (long long)rep->recv_bad_ids);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,507 @@
+// Routing, slot assignment and row-movement kernels of libmoe (gfx950).
+//
+// Slot assignment is a deterministic two-pass scan: one 256-thread block
+// ranks SCAN_CHUNK keys with wave64 ballots (equal keys are peeled one value
+// at a time: ballot -> popcount of lower lanes), then one block per key
+// value scans the per-chunk counts.  No atomics.
+
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ top-k
+
+// One wave per token: k rounds of a wave-wide (value desc, index asc) argmax.
+template <int EPL>
+__global__ void __launch_bounds__(256)
+select_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx,
+                   float* __restrict__ w) {
+  const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const int lane = lane_id();
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  float v[EPL];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? row[e] : 0.f;
+    if (e >= E) taken |= 1u << j;
+  }
+  float my_v = 0.f, v0 = 0.f;
+  int my_i = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = 0.f;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      if (!((taken >> j) & 1u) && (bi == 0x7fffffff || v[j] > bv || (v[j] == bv && e < bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      const bool better = (oi != 0x7fffffff) && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
+      if (better) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (r == 0) v0 = bv;
+    if (lane == r) {
+      my_v = bv;
+      my_i = bi;
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+  }
+  float ex = lane < k ? expf(my_v - v0) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane < k) {
+    idx[(int64_t)t * k + lane] = my_i;
+    w[(int64_t)t * k + lane] = ex / sum;
+  }
+}
+
+hipError_t launch_select_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t st) {
+  const int epl = (E + 63) / 64;
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (T == 0) return hipSuccess;
+#define SEL(N) hipLaunchKernelGGL(select_topk_kernel<N>, grid, block, 0, st, logits, T, E, k, idx, w)
+  if (epl <= 1) SEL(1);
+  else if (epl <= 2) SEL(2);
+  else if (epl <= 4) SEL(4);
+  else if (epl <= 6) SEL(6);
+  else if (epl <= 8) SEL(8);
+  else if (epl <= 16) SEL(16);
+  else SEL(32);
+#undef SEL
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ chunk ranking
+
+// Rank of each lane's key among the lanes of this wave with the same key,
+// offset by the running count run[key] (wave-private LDS), which is advanced.
+// key < 0: no key.  All lanes of the wave must call this together.
+__device__ __forceinline__ int peel_rank(int key, int32_t* run) {
+  int rank = 0;
+  uint64_t active = __ballot(key >= 0);
+  const uint64_t lt = lanemask_lt();
+  while (active) {
+    const int leader = __builtin_ctzll(active);
+    const int kk = __shfl(key, leader);
+    const uint64_t m = __ballot(key == kk);
+    const int before = run[kk];
+    if (key == kk) rank = before + __popcll(m & lt);
+    if (lane_id() == leader) run[kk] = before + __popcll(m);
+    active &= ~m;
+  }
+  return rank;
+}
+
+// Block-wide: rank 1024 keys (4 waves x 4 x 64) inside the chunk; write each
+// key's chunk-local rank and the per-key chunk count (column-major: [key][chunk]).
+// key values in [0, KW).  get_key(i) returns -1 for "no key".
+template <class GetKey>
+__device__ __forceinline__ void chunk_rank(GetKey get_key, int n, int KW, int nch, int32_t* run_all,
+                                           int32_t* __restrict__ local_rank, int32_t* __restrict__ chunk_count,
+                                           int32_t* __restrict__ key_out) {
+  for (int i = threadIdx.x; i < 4 * KW; i += 256) run_all[i] = 0;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  int32_t* run = run_all + wave * KW;
+  const int base = blockIdx.x * SCAN_CHUNK + wave * 256;
+  int key[4], rk[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int i = base + it * 64 + lane;
+    key[it] = i < n ? get_key(i) : -1;
+    rk[it] = peel_rank(key[it], run);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int i = base + it * 64 + lane;
+    if (i < n) {
+      if (key_out) key_out[i] = key[it];
+      if (key[it] >= 0) {
+        int off = 0;
+        for (int w = 0; w < wave; ++w) off += run_all[w * KW + key[it]];
+        local_rank[i] = off + rk[it];
+      }
+    }
+  }
+  for (int kk = threadIdx.x; kk < KW; kk += 256)
+    chunk_count[(int64_t)kk * nch + blockIdx.x] =
+        run_all[kk] + run_all[KW + kk] + run_all[2 * KW + kk] + run_all[3 * KW + kk];
+}
+
+// Exclusive scan of one key's chunk counts (one block per key column).
+// Returns the column total to every thread.
+__device__ __forceinline__ int column_scan(const int32_t* __restrict__ col_in, int32_t* __restrict__ col_out,
+                                           int nch) {
+  __shared__ int32_t part[256];
+  const int per = (nch + 255) / 256;
+  const int c0 = threadIdx.x * per;
+  int s = 0;
+  for (int c = c0; c < c0 + per && c < nch; ++c) s += col_in[c];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over 256 partial sums
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - s;
+  for (int c = c0; c < c0 + per && c < nch; ++c) {
+    const int v = col_in[c];
+    col_out[c] = run;
+    run += v;
+  }
+  const int total = part[255];
+  __syncthreads();
+  return total;
+}
+
+// ------------------------------------------------------------------ send
+
+__global__ void __launch_bounds__(256)
+send_rank_kernel(const int32_t* __restrict__ idx, int n_assign, int X, int E, int R,
+                 int32_t* __restrict__ local_rank, int32_t* __restrict__ chunk_count, int nch) {
+  extern __shared__ int32_t run_all[];
+  auto key = [&](int a) {
+    const int e = idx[a];
+    return (e >= 0 && e < E) ? e / X : R;  // R: invalid expert id
+  };
+  chunk_rank(key, n_assign, R + 1, nch, run_all, local_rank, chunk_count, nullptr);
+}
+
+hipError_t launch_send_rank(const int32_t* idx, int n_assign, int X, int E, int R, int32_t* local_rank,
+                            int32_t* chunk_count, hipStream_t st) {
+  const int nch = (n_assign + SCAN_CHUNK - 1) / SCAN_CHUNK;
+  if (nch == 0) return hipSuccess;
+  hipLaunchKernelGGL(send_rank_kernel, dim3(nch), dim3(256), 4 * (R + 1) * sizeof(int32_t), st, idx, n_assign,
+                     X, E, R, local_rank, chunk_count, nch);
+  return hipGetLastError();
+}
+
+// Block d scans destination d's chunk counts; writes demand, kept count.
+__global__ void __launch_bounds__(256)
+send_scan_kernel(const int32_t* __restrict__ chunk_count, int nch, int R, int cap, int32_t* __restrict__ chunk_base,
+                 int32_t* __restrict__ ctr, int32_t* __restrict__ send_count_out) {
+  const int d = blockIdx.x;
+  const int total = column_scan(chunk_count + (int64_t)d * nch, chunk_base + (int64_t)d * nch, nch);
+  if (threadIdx.x == 0) {
+    if (d < R) {
+      const int kept = min(total, cap);
+      ctr[Ctr::HEADER + d] = total;
+      ctr[Ctr::HEADER + R + d] = kept;
+      send_count_out[d] = kept;
+    } else {
+      ctr[Ctr::SEND_INVALID] = total;
+    }
+  }
+}
+
+hipError_t launch_send_scan(const int32_t* chunk_count, int nch, int R, int cap, int32_t* chunk_base, int32_t* ctr,
+                            int32_t* send_count_out, hipStream_t st) {
+  // nch == 0 (no tokens) still runs: every column total is 0
+  hipLaunchKernelGGL(send_scan_kernel, dim3(R + 1), dim3(256), 0, st, chunk_count, nch, R, cap, chunk_base, ctr,
+                     send_count_out);
+  return hipGetLastError();
+}
+
+// One block per token: work out the k slots, then copy the latent row once
+// from HBM into every kept destination row (16 bytes per lane, coalesced).
+// Blocks past T mark the empty slots of every pool with id -1.
+constexpr int PACK_TPB = 128;
+
+__global__ void __launch_bounds__(PACK_TPB)
+pack_kernel(const char* __restrict__ z, int64_t row_bytes, const int32_t* __restrict__ idx,
+            const int32_t* __restrict__ local_rank, const int32_t* __restrict__ chunk_base, int nch, int T, int k,
+            int X, int E, int R, int cap, char* __restrict__ pools, int64_t dst_stride, int64_t prow,
+            int32_t* __restrict__ slot_of, const int32_t* __restrict__ send_count) {
+  const int t = blockIdx.x;
+  if (t >= T) {
+    // empty-slot ids: slots [send_count[d], cap) of every pool d
+    const int64_t i = (int64_t)(t - T) * PACK_TPB + threadIdx.x;
+    if (i < (int64_t)R * cap) {
+      const int d = (int)(i / cap), s = (int)(i - (int64_t)d * cap);
+      if (s >= send_count[d]) *(int32_t*)(pools + d * dst_stride + s * prow + row_bytes) = -1;
+    }
+    return;
+  }
+  __shared__ int64_t off[32];
+  __shared__ int32_t ids[32];
+  if (threadIdx.x < k) {
+    const int64_t a = (int64_t)t * k + threadIdx.x;
+    const int e = idx[a];
+    int64_t o = -1;
+    int slot = -1;
+    if (e >= 0 && e < E) {
+      const int d = e / X;
+      const int r = chunk_base[(int64_t)d * nch + (int)(a / SCAN_CHUNK)] + local_rank[a];
+      if (r < cap) {
+        slot = d * cap + r;
+        o = d * dst_stride + (int64_t)r * prow;
+      }
+    }
+    slot_of[a] = slot;
+    off[threadIdx.x] = o;
+    ids[threadIdx.x] = e;
+  }
+  __syncthreads();
+  const uint4* src = (const uint4*)(z + (int64_t)t * row_bytes);
+  const int nchunk = (int)(row_bytes >> 4);
+  for (int c = threadIdx.x; c < nchunk; c += PACK_TPB) {
+    const uint4 v = src[c];
+    for (int i = 0; i < k; ++i)
+      if (off[i] >= 0) ((uint4*)(pools + off[i]))[c] = v;
+  }
+  if (threadIdx.x < k && off[threadIdx.x] >= 0)
+    *(int32_t*)(pools + off[threadIdx.x] + row_bytes) = ids[threadIdx.x];
+}
+
+hipError_t launch_pack(const void* z, int64_t row_bytes, const int32_t* idx, const int32_t* local_rank,
+                       const int32_t* chunk_base, int T, int k, int X, int E, int R, int cap, void* pools,
+                       int64_t dst_stride, int64_t prow, int32_t* slot_of, const int32_t* send_count, hipStream_t st) {
+  const int nch = (T * k + SCAN_CHUNK - 1) / SCAN_CHUNK;
+  const int64_t fill_blocks = ((int64_t)R * cap + PACK_TPB - 1) / PACK_TPB;
+  const int64_t blocks = (int64_t)T + fill_blocks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(PACK_TPB), 0, st, (const char*)z, row_bytes, idx,
+                     local_rank, chunk_base, nch, T, k, X, E, R, cap, (char*)pools, dst_stride, prow, slot_of,
+                     send_count);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- receive
+
+__global__ void __launch_bounds__(256)
+recv_rank_kernel(const char* __restrict__ pools, int64_t src_stride, int64_t prow, int64_t id_off, int n_rows,
+                 int cap, int X, int my_rank, int32_t* __restrict__ row_j, int32_t* __restrict__ row_lrank,
+                 int32_t* __restrict__ chunk_count, int nch) {
+  extern __shared__ int32_t run_all[];
+  auto key = [&](int row) {
+    const int s = row / cap, sl = row - s * cap;
+    const int e = *(const int32_t*)(pools + s * src_stride + (int64_t)sl * prow + id_off);
+    if (e < 0) return -1;
+    const int j = e - X * my_rank;
+    return (j >= 0 && j < X) ? j : X;  // X: id of another rank's expert
+  };
+  chunk_rank(key, n_rows, X + 1, nch, run_all, row_lrank, chunk_count, row_j);
+}
+
+hipError_t launch_recv_rank(const void* pools, int64_t src_stride, int64_t prow, int64_t id_off, int R, int cap,
+                            int X, int my_rank, int32_t* row_j, int32_t* row_lrank, int32_t* chunk_count,
+                            hipStream_t st) {
+  const int n_rows = R * cap;
+  const int nch = (n_rows + SCAN_CHUNK - 1) / SCAN_CHUNK;
+  if (nch == 0) return hipSuccess;
+  hipLaunchKernelGGL(recv_rank_kernel, dim3(nch), dim3(256), 4 * (X + 1) * sizeof(int32_t), st,
+                     (const char*)pools, src_stride, prow, id_off, n_rows, cap, X, my_rank, row_j, row_lrank,
+                     chunk_count, nch);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256)
+recv_scan_kernel(const int32_t* __restrict__ chunk_count, int nch, int X, int rcap, int j0, int nj,
+                 int32_t* __restrict__ chunk_base, int32_t* __restrict__ arrivals, int32_t* __restrict__ kept,
+                 int32_t* __restrict__ bad, int32_t* __restrict__ wave_count) {
+  const int j = blockIdx.x;
+  const int total = column_scan(chunk_count + (int64_t)j * nch, chunk_base + (int64_t)j * nch, nch);
+  if (threadIdx.x == 0) {
+    if (j < X) {
+      const int kp = min(total, rcap);
+      arrivals[j] = total;
+      kept[j] = kp;
+      if (j >= j0 && j < j0 + nj) wave_count[j - j0] = kp;
+    } else {
+      *bad = total;
+    }
+  }
+}
+
+hipError_t launch_recv_scan(const int32_t* chunk_count, int nch, int X, int rcap, int j0, int nj,
+                            int32_t* chunk_base, int32_t* arrivals, int32_t* kept, int32_t* bad,
+                            int32_t* wave_count, hipStream_t st) {
+  hipLaunchKernelGGL(recv_scan_kernel, dim3(X + 1), dim3(256), 0, st, chunk_count, nch, X, rcap, j0, nj,
+                     chunk_base, arrivals, kept, bad, wave_count);
+  return hipGetLastError();
+}
+
+// Thread i: (a) final rank of receive row i, its row_src entry if it is kept
+// by an expert of this wave; (b) row_src slot i of the wave set to -1 if it
+// lies past that expert's count.
+__global__ void __launch_bounds__(256)
+recv_place_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict__ row_lrank,
+                  const int32_t* __restrict__ chunk_base, int nch, int n_rows, int X, int rcap, int j0, int nj,
+                  const int32_t* __restrict__ wave_count, int32_t* __restrict__ row_rank,
+                  int32_t* __restrict__ row_src) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n_rows) {
+    const int j = row_j[i];
+    int rank = -1;
+    if (j >= 0 && j < X) {
+      rank = chunk_base[(int64_t)j * nch + i / SCAN_CHUNK] + row_lrank[i];
+      if (j >= j0 && j < j0 + nj && rank < rcap) row_src[(int64_t)(j - j0) * rcap + rank] = i;
+    }
+    row_rank[i] = rank;
+  }
+  if (i < nj * rcap) {
+    const int jw = i / rcap, r = i - jw * rcap;
+    if (r >= wave_count[jw]) row_src[i] = -1;
+  }
+}
+
+hipError_t launch_recv_place(const int32_t* row_j, const int32_t* row_lrank, const int32_t* chunk_base, int n_rows,
+                             int X, int rcap, int j0, int nj, const int32_t* wave_count, int32_t* row_rank,
+                             int32_t* row_src, hipStream_t st) {
+  const int nch = (n_rows + SCAN_CHUNK - 1) / SCAN_CHUNK;
+  const int n = max(n_rows, nj * rcap);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(recv_place_kernel, dim3((n + 255) / 256), dim3(256), 0, st, row_j, row_lrank, chunk_base, nch,
+                     n_rows, X, rcap, j0, nj, wave_count, row_rank, row_src);
+  return hipGetLastError();
+}
+
+// One wave per wave-buffer row: copy the kept pool row (payload only).
+__global__ void __launch_bounds__(256)
+wave_gather_kernel(const char* __restrict__ pools, int64_t src_stride, int64_t prow, int cap, int64_t row_bytes,
+                   const int32_t* __restrict__ row_src, const int32_t* __restrict__ wave_count, int nj, int rcap,
+                   char* __restrict__ wave_buf) {
+  const int64_t r_all = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r_all >= (int64_t)nj * rcap) return;
+  const int jw = (int)(r_all / rcap), r = (int)(r_all - (int64_t)jw * rcap);
+  if (r >= wave_count[jw]) return;
+  const int rs = row_src[r_all];
+  const int s = rs / cap, sl = rs - s * cap;
+  const uint4* src = (const uint4*)(pools + s * src_stride + (int64_t)sl * prow);
+  uint4* dst = (uint4*)(wave_buf + r_all * row_bytes);
+  const int nchunk = (int)(row_bytes >> 4);
+  for (int c = lane_id(); c < nchunk; c += 64) dst[c] = src[c];
+}
+
+hipError_t launch_wave_gather(const void* pools, int64_t src_stride, int64_t prow, int cap, int64_t row_bytes,
+                              const int32_t* row_src, const int32_t* wave_count, int nj, int rcap, void* wave_buf,
+                              hipStream_t st) {
+  const int64_t rows = (int64_t)nj * rcap;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(wave_gather_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, (const char*)pools,
+                     src_stride, prow, cap, row_bytes, row_src, wave_count, nj, rcap, (char*)wave_buf);
+  return hipGetLastError();
+}
+
+// One wave per receive row: a row of this wave's experts that did not fit
+// gets an all-zero return row.
+__global__ void __launch_bounds__(256)
+zero_dropped_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict__ row_rank, int n_rows, int cap,
+                    int rcap, int j0, int nj, char* __restrict__ ret, int64_t ret_src_stride, int64_t row_bytes) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  const int j = row_j[row];
+  if (j < j0 || j >= j0 + nj || row_rank[row] < rcap) return;
+  const int s = row / cap, sl = row - s * cap;
+  uint4* dst = (uint4*)(ret + s * ret_src_stride + (int64_t)sl * row_bytes);
+  const int nchunk = (int)(row_bytes >> 4);
+  for (int c = lane_id(); c < nchunk; c += 64) dst[c] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero_dropped(const int32_t* row_j, const int32_t* row_rank, int n_rows, int cap, int rcap, int j0,
+                               int nj, void* ret, int64_t ret_src_stride, int64_t row_bytes, hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_dropped_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, st, row_j, row_rank, n_rows, cap,
+                     rcap, j0, nj, (char*)ret, ret_src_stride, row_bytes);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- combine
+
+template <class T> struct Vec8;
+template <> struct Vec8<bf16_t> {
+  __device__ static void load(const bf16_t* p, float* f) {
+    const uint4 u = *(const uint4*)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(bf16_t* p, const float* f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct Vec8<float> {
+  __device__ static void load(const float* p, float* f) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  __device__ static void store(float* p, const float* f) {
+    *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
+    *(float4*)(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+};
+
+constexpr int COMBINE_TPB = 128;
+
+// One block per token: c = act(sum_i w_i * returned row i), i ascending, fp32.
+template <class T>
+__global__ void __launch_bounds__(COMBINE_TPB)
+combine_kernel(const char* __restrict__ ret, int64_t dst_stride, int64_t row_bytes, int cap,
+               const int32_t* __restrict__ slot_of, const float* __restrict__ w, int k, int L,
+               T* __restrict__ c_out, int64_t ldc) {
+  const int t = blockIdx.x;
+  __shared__ int64_t off[32];
+  __shared__ float ww[32];
+  if (threadIdx.x < k) {
+    const int s = slot_of[(int64_t)t * k + threadIdx.x];
+    int64_t o = -1;
+    if (s >= 0) {
+      const int d = s / cap, sl = s - d * cap;
+      o = d * dst_stride + (int64_t)sl * row_bytes;
+    }
+    off[threadIdx.x] = o;
+    ww[threadIdx.x] = w[(int64_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < L / 8; c += COMBINE_TPB) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < k; ++i) {
+      if (off[i] < 0) continue;
+      float f[8];
+      Vec8<T>::load((const T*)(ret + off[i]) + c * 8, f);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(ww[i], f[q], acc[q]);
+    }
+    Vec8<T>::store(c_out + (int64_t)t * ldc + c * 8, acc);
+  }
+}
+
+hipError_t launch_combine(int act, const void* ret, int64_t dst_stride, int64_t row_bytes, int cap,
+                          const int32_t* slot_of, const float* w, int T, int k, int L, void* c_out, int64_t ldc,
+                          hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (act == 0)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(COMBINE_TPB), 0, st, (const char*)ret, dst_stride,
+                       row_bytes, cap, slot_of, w, k, L, (bf16_t*)c_out, ldc);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(COMBINE_TPB), 0, st, (const char*)ret, dst_stride,
+                       row_bytes, cap, slot_of, w, k, L, (float*)c_out, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,54 @@
+// Internal launchers of libmoe (host side).  Kernels live in kernels.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Assignments (send side) and pool rows (receive side) are ranked in chunks
+// of SCAN_CHUNK by one 256-thread block each, then the chunk counts are
+// scanned by one block.  No atomics anywhere: results are deterministic.
+constexpr int SCAN_CHUNK = 1024;
+
+// Workspace counter block (int32 words).
+struct Ctr {
+  static constexpr int SEND_DROPPED = 0;
+  static constexpr int SEND_INVALID = 1;
+  static constexpr int RECV_BAD = 2;
+  static constexpr int HEADER = 16;
+  // then: demand[R], send_count[R], arrivals[X], kept[X]
+};
+
+hipError_t launch_select_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                              hipStream_t st);
+
+hipError_t launch_send_rank(const int32_t* idx, int n_assign, int X, int E, int R, int32_t* local_rank,
+                            int32_t* chunk_count, hipStream_t st);
+hipError_t launch_send_scan(const int32_t* chunk_count, int nch, int R, int cap, int32_t* chunk_base,
+                            int32_t* ctr, int32_t* send_count_out, hipStream_t st);
+hipError_t launch_pack(const void* z, int64_t row_bytes, const int32_t* idx, const int32_t* local_rank,
+                       const int32_t* chunk_base, int T, int k, int X, int E, int R, int cap, void* pools,
+                       int64_t dst_stride, int64_t pool_row_stride, int32_t* slot_of, const int32_t* send_count,
+                       hipStream_t st);
+
+hipError_t launch_recv_rank(const void* pools, int64_t src_stride, int64_t pool_row_stride, int64_t id_off,
+                            int R, int cap, int X, int my_rank, int32_t* row_j, int32_t* row_lrank,
+                            int32_t* chunk_count, hipStream_t st);
+hipError_t launch_recv_scan(const int32_t* chunk_count, int nch, int X, int rcap, int j0, int nj,
+                            int32_t* chunk_base, int32_t* ctr_arrivals, int32_t* ctr_kept, int32_t* ctr_bad,
+                            int32_t* wave_count, hipStream_t st);
+hipError_t launch_recv_place(const int32_t* row_j, const int32_t* row_lrank, const int32_t* chunk_base,
+                             int n_rows, int X, int rcap, int j0, int nj, const int32_t* wave_count,
+                             int32_t* row_rank, int32_t* row_src, hipStream_t st);
+hipError_t launch_wave_gather(const void* pools, int64_t src_stride, int64_t pool_row_stride, int cap,
+                              int64_t row_bytes, const int32_t* row_src, const int32_t* wave_count, int nj,
+                              int rcap, void* wave_buf, hipStream_t st);
+hipError_t launch_zero_dropped(const int32_t* row_j, const int32_t* row_rank, int n_rows, int cap, int rcap,
+                               int j0, int nj, void* ret, int64_t ret_src_stride, int64_t row_bytes,
+                               hipStream_t st);
+hipError_t launch_combine(int act, const void* ret, int64_t dst_stride, int64_t row_bytes, int cap,
+                          const int32_t* slot_of, const float* w, int T, int k, int L, void* c_out,
+                          int64_t ldc, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,209 @@
+"""Device buffers and the call sequence of the MoE layer on one GPU.
+
+torch provides device memory, copies and streams; every step of the layer is
+a libmoe call (see binding.py).  Two layouts of the expert-parallel domain
+are provided:
+
+* ``OneRankLayer``: one rank's share at its real shape.  The rank's own
+  tokens go through route -> pack; its receive buffer holds its own pool for
+  itself plus the pools the other ranks sent (inputs); its combine reads the
+  rows it computed for itself plus the rows the other ranks returned
+  (inputs).  The only copies are the self-blocks of the two exchanges.
+* ``AllRanksLayer``: every rank of a small domain on one device.  All send
+  pools sit in one [R_src][R_dst][send_cap][stride] block and all return rows
+  in one [R_recv][R_src][send_cap][L] block, so each exchange is a strided
+  view: zero copies.
+"""
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def upload(arr, device):
+    """Host storage array (uint16 bf16 bit patterns or float32) -> device tensor."""
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if a.dtype == np.float32:
+        return torch.from_numpy(a).to(device)
+    if a.dtype == np.int32:
+        return torch.from_numpy(a).to(device)
+    raise TypeError(f"unsupported host dtype {a.dtype}")
+
+
+def _act(shape):
+    return torch.bfloat16 if shape.act == "bf16" else torch.float32
+
+
+def pool_block_host(ids, rows, prow, act):
+    """Host bytes of pools in the row layout of moe_pack_pools: [n][cap][prow]."""
+    n, cap = ids.shape
+    L = rows.shape[-1]
+    esize = 2 if act == "bf16" else 4
+    out = np.zeros((n, cap, prow), dtype=np.uint8)
+    payload = np.ascontiguousarray(rows).view(np.uint8).reshape(n, cap, L * esize)
+    out[:, :, :L * esize] = payload
+    out[:, :, L * esize:L * esize + 4] = np.ascontiguousarray(ids, dtype=np.int32).view(np.uint8).reshape(n, cap, 4)
+    return out
+
+
+class OneRankLayer:
+    """One EP rank's layer.  ``inp`` is a workload.gen.generate() dict."""
+
+    def __init__(self, shape, inp, device="cuda", gather="fused"):
+        self.shape, self.device = shape, device
+        self.gather = gather
+        r = int(inp["receiver"])
+        self.rank = r
+        self.dims = B.make_dims(shape, my_rank=r)
+        self.scap, self.rcap, self.prow = B.capacity(self.dims)
+        T, D, L, E, k, R = shape.tokens, shape.d_model, shape.latent, shape.n_experts, shape.top_k, shape.n_ranks
+        X, W, H = shape.local_experts, shape.waves, shape.expert_hidden
+        WX = X // W
+        act = _act(shape)
+        dev = device
+        self.full = shape.layer == "full"
+        # inputs
+        self.x = upload(inp["x"], dev)
+        self.w_router = upload(inp["w_router"], dev)
+        self.w_down = upload(inp["w_down"], dev)
+        self.bias = None if inp["bias"] is None else upload(np.ascontiguousarray(inp["bias"], np.float32), dev)
+        self.bias_row_tokens = int(inp["bias_row_tokens"])
+        # route / pack outputs
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.z = torch.empty((T, L), dtype=act, device=dev)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.send_pools = torch.empty((R, self.scap, self.prow), dtype=torch.uint8, device=dev)
+        self.slot_of = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.send_count = torch.empty((R,), dtype=torch.int32, device=dev)
+        # receive side: pools from the other ranks are inputs; slot r is our own pool
+        self.recv_pools = upload(pool_block_host(inp["foreign_ids"], inp["foreign_rows"], self.prow, shape.act), dev)
+        self.row_src = torch.empty((W, WX, self.rcap), dtype=torch.int32, device=dev)
+        self.wave_count = torch.empty((W, WX), dtype=torch.int32, device=dev)
+        self.wave_buf = torch.empty((WX, self.rcap, L), dtype=act, device=dev) if gather == "buffer" else None
+        self.ws = torch.empty((B.workspace_size(self.dims),), dtype=torch.uint8, device=dev)
+        if self.full:
+            self.w13 = upload(inp["w13"], dev)
+            self.w2 = upload(inp["w2"], dev)
+            self.w_up = upload(inp["w_up"], dev)
+            self.ws13 = upload(inp["ws13"], dev)
+            self.ws2 = upload(inp["ws2"], dev)
+            self.ret_send = torch.zeros((R, self.scap, L), dtype=act, device=dev)
+            self.ret_recv = upload(inp["foreign_ret"], dev)
+            self.out = torch.empty((T, D), dtype=act, device=dev)
+
+    @property
+    def esize(self):
+        return 2 if self.shape.act == "bf16" else 4
+
+    def dispatch(self, stream=None):
+        d = self.dims
+        B.route(d, self.x, self.w_router, self.w_down, self.bias, self.bias_row_tokens, self.logits, self.z,
+                self.idx, self.w, self.ws, stream)
+        B.pack_pools(d, self.z, self.idx, self.send_pools, self.scap * self.prow, self.slot_of,
+                     self.send_count, self.ws, stream)
+        # self-block of the dispatch exchange
+        self.recv_pools[self.rank].copy_(self.send_pools[self.rank])
+
+    def receive_wave(self, w, stream=None):
+        B.recv_waves(self.dims, self.recv_pools, self.scap * self.prow, w, self.wave_buf, self.row_src[w],
+                     self.wave_count[w], self.ws, stream)
+
+    def expert_wave(self, w, stream=None):
+        B.expert_gemm(self.dims, w, self.wave_buf, self.recv_pools, self.scap * self.prow, self.row_src[w],
+                      self.wave_count[w], self.w13, self.w2, self.ret_send, self.scap * self.shape.latent * self.esize,
+                      self.ws, stream)
+
+    def combine(self, stream=None):
+        # self-block of the return exchange
+        self.ret_recv[self.rank].copy_(self.ret_send[self.rank])
+        B.combine(self.dims, self.ret_recv, self.scap * self.shape.latent * self.esize, self.slot_of, self.w,
+                  self.w_up, self.x, self.ws13, self.ws2, self.out, self.ws, stream)
+
+    def run(self, stream=None):
+        self.dispatch(stream)
+        for w in range(self.shape.waves):
+            self.receive_wave(w, stream)
+            if self.full:
+                self.expert_wave(w, stream)
+        if self.full:
+            self.combine(stream)
+
+    def drop_report(self, stream=None):
+        return B.drop_stats(self.dims, self.ws, stream, raise_on_bad_ids=False).as_dict()
+
+
+class AllRanksLayer:
+    """Every rank of a small EP domain on one device (zero-copy exchanges)."""
+
+    def __init__(self, shape, inp, device="cuda", gather="fused"):
+        self.shape, self.device, self.gather = shape, device, gather
+        T, D, L, E, k, R = shape.tokens, shape.d_model, shape.latent, shape.n_experts, shape.top_k, shape.n_ranks
+        X, W = shape.local_experts, shape.waves
+        WX = X // W
+        act = _act(shape)
+        dev = device
+        self.dims = [B.make_dims(shape, my_rank=r) for r in range(R)]
+        self.scap, self.rcap, self.prow = B.capacity(self.dims[0])
+        self.x = upload(inp["x"], dev)                                  # [R][T][D]
+        self.w_router = upload(inp["w_router"], dev)
+        self.w_down = upload(inp["w_down"], dev)
+        bias = inp["bias"]
+        if bias is not None and bias.ndim == 2:
+            bias = np.broadcast_to(bias, (R,) + bias.shape)
+        self.bias = None if bias is None else upload(np.ascontiguousarray(bias, np.float32), dev)
+        self.bias_row_tokens = int(inp["bias_row_tokens"])
+        self.w13 = upload(inp["w13"], dev)                              # [E][2H][L]
+        self.w2 = upload(inp["w2"], dev)                                # [E][L][H]
+        self.w_up = upload(inp["w_up"], dev)
+        self.ws13 = upload(inp["ws13"], dev)
+        self.ws2 = upload(inp["ws2"], dev)
+        self.logits = torch.empty((R, T, E), dtype=torch.float32, device=dev)
+        self.z = torch.empty((R, T, L), dtype=act, device=dev)
+        self.idx = torch.empty((R, T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((R, T, k), dtype=torch.float32, device=dev)
+        self.pools = torch.empty((R, R, self.scap, self.prow), dtype=torch.uint8, device=dev)   # [src][dst]
+        self.slot_of = torch.empty((R, T, k), dtype=torch.int32, device=dev)
+        self.send_count = torch.empty((R, R), dtype=torch.int32, device=dev)
+        self.row_src = torch.empty((R, W, WX, self.rcap), dtype=torch.int32, device=dev)
+        self.wave_count = torch.empty((R, W, WX), dtype=torch.int32, device=dev)
+        self.wave_buf = torch.empty((WX, self.rcap, L), dtype=act, device=dev) if gather == "buffer" else None
+        self.ret = torch.zeros((R, R, self.scap, L), dtype=act, device=dev)                     # [recv][src]
+        self.out = torch.empty((R, T, D), dtype=act, device=dev)
+        self.ws = [torch.empty((B.workspace_size(self.dims[0]),), dtype=torch.uint8, device=dev)
+                   for _ in range(R)]
+
+    def run(self, stream=None):
+        sh = self.shape
+        R, L = sh.n_ranks, sh.latent
+        esize = 2 if sh.act == "bf16" else 4
+        pool_bytes = self.scap * self.prow
+        for s in range(R):
+            d = self.dims[s]
+            bias = None if self.bias is None else self.bias[s]
+            B.route(d, self.x[s], self.w_router, self.w_down, bias, self.bias_row_tokens, self.logits[s],
+                    self.z[s], self.idx[s], self.w[s], self.ws[s], stream)
+            B.pack_pools(d, self.z[s], self.idx[s], self.pools[s], pool_bytes, self.slot_of[s],
+                         self.send_count[s], self.ws[s], stream)
+        X = sh.local_experts
+        for r in range(R):
+            d = self.dims[r]
+            recv_view = self.pools[0, r]                 # pool from source s at + s * R * pool_bytes
+            for w in range(sh.waves):
+                B.recv_waves(d, recv_view, R * pool_bytes, w, self.wave_buf, self.row_src[r, w],
+                             self.wave_count[r, w], self.ws[r], stream)
+                B.expert_gemm(d, w, self.wave_buf, recv_view, R * pool_bytes, self.row_src[r, w],
+                              self.wave_count[r, w], self.w13[r * X:(r + 1) * X], self.w2[r * X:(r + 1) * X],
+                              self.ret[r], self.scap * L * esize, self.ws[r], stream)
+        for s in range(R):
+            d = self.dims[s]
+            ret_view = self.ret[0, s]                    # rows from receiver d at + d * R * scap * L
+            B.combine(d, ret_view, R * self.scap * L * esize, self.slot_of[s], self.w[s], self.w_up, self.x[s],
+                      self.ws13, self.ws2, self.out[s], self.ws[s], stream)
+
+    def drop_reports(self, stream=None):
+        return [B.drop_stats(self.dims[r], self.ws[r], stream, raise_on_bad_ids=False).as_dict()
+                for r in range(self.shape.n_ranks)]

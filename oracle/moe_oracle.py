@@ -182,7 +182,7 @@ def pack_pools(idx, slot_of, R, send_cap, z=None):
         rows = np.zeros((R * send_cap, z.shape[1]), dtype=np.float64)
         tok = np.repeat(np.arange(T), k)[keep]
         rows[flat_slot[keep]] = z[tok]
-        rows = rows.reshape(R, send_cap, -1)
+        rows = rows.reshape(R, send_cap, z.shape[1])
     return ids.reshape(R, send_cap), rows
 
 

@@ -1,0 +1,273 @@
+"""GPU parity: libmoe (through its C ABI) against the CPU oracle.
+
+Small layers: every rank of the EP domain is emulated on one device and the
+whole layer is compared element by element (routing, slots, pools, receive
+ranks, drop ledgers exactly; floats to the tolerances of parity_util).
+Full-size layers (configs 2-5): one rank's share in the launch configuration
+the benchmark times; routing, slots, pools, receive ranks and drops exactly,
+floating-point outputs on sampled tokens and rows.
+"""
+
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from workload import configs, gen
+from parity_util import assert_bar, assert_stored_close, host, unambiguous_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def runner():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from grouped_expert_ffn_router_amd import runner as R
+    return R
+
+
+def _shape(name):
+    return configs.get(1) if name == "cfg1" else configs.get(name)
+
+
+def _decode_pools(pools_u8, L, act):
+    """[..., cap, prow] uint8 -> (ids [..., cap] int32, payload [..., cap, L] float64)."""
+    a = pools_u8.cpu().numpy()
+    es = 2 if act == "bf16" else 4
+    ids = np.ascontiguousarray(a[..., L * es:L * es + 4]).view(np.int32)[..., 0]
+    pay = np.ascontiguousarray(a[..., :L * es])
+    if act == "bf16":
+        vals = gen.bf16_bits_to_f32(pay.view(np.uint16)).astype(np.float64)
+    else:
+        vals = pay.view(np.float32).astype(np.float64)
+    return ids, vals
+
+
+def _check_routing(sh, ref_d, gl, gidx, gw, grid, what):
+    ol = ref_d["logits"]
+    if grid:
+        assert np.array_equal(gl, ol), f"{what}: logits differ on the exact grid"
+    else:
+        mask, delta = unambiguous_tokens(ol, gl, sh.top_k)
+        assert delta < 1e-3, f"{what}: logit difference {delta}"
+        assert mask.all(), f"{what}: {int((~mask).sum())} tokens have near-tied logits; use the exact grid"
+    assert np.array_equal(gidx, ref_d["idx"]), f"{what}: topk_idx differs"
+    np.testing.assert_allclose(gw, ref_d["w"], atol=1e-5, rtol=0, err_msg=f"{what}: topk_w")
+
+
+ALL = ["cfg1", "mini_bf16", "mini_bf16_skew", "mini_bf16_seg", "mini_f32"]
+
+
+@pytest.mark.parametrize("gather", ["fused", "buffer"])
+@pytest.mark.parametrize("grid", [True, False])
+@pytest.mark.parametrize("name", ALL)
+def test_all_ranks_layer(runner, name, grid, gather):
+    sh = _shape(name)
+    seed = 11 if grid else 12
+    _say(f"[all-ranks] {name} grid={grid} gather={gather} seed={seed}")
+    inp = gen.generate(sh, seed=seed, grid=grid)
+    ref = O.layer_all_ranks(sh, inp)
+    lay = runner.AllRanksLayer(sh, inp, gather=gather)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, grid)
+
+
+def _check_all_ranks(sh, inp, ref, lay, grid):
+    R, L, act, X, W = sh.n_ranks, sh.latent, sh.act, sh.local_experts, sh.waves
+    scap, rcap = ref["send_cap"], ref["recv_cap"]
+    assert (lay.scap, lay.rcap) == (scap, rcap)
+    reps = lay.drop_reports()
+    pool_ids, pool_rows = _decode_pools(lay.pools, L, act)           # [src][dst][cap]
+    for s in range(R):
+        d = ref["dispatch"][s]
+        _check_routing(sh, d, host(lay.logits[s]), host(lay.idx[s]), host(lay.w[s]), grid, f"src {s}")
+        gz = host(lay.z[s])
+        if grid:
+            assert np.array_equal(gz, d["z"]), f"src {s}: z differs on the grid"
+        else:
+            assert_stored_close(gz, d["z"], act, f"src {s} z")
+        assert np.array_equal(host(lay.slot_of[s]), d["slot_of"]), f"src {s}: slot_of"
+        assert np.array_equal(host(lay.send_count[s]), d["send_count"]), f"src {s}: send_count"
+        assert np.array_equal(pool_ids[s], d["pool_ids"]), f"src {s}: pool ids"
+        # payload rows are the GPU's own z rows (pure data movement: exact)
+        so = d["slot_of"].reshape(-1)
+        tok = np.repeat(np.arange(sh.tokens), sh.top_k)
+        ok = so >= 0
+        flat_rows = pool_rows[s].reshape(R * scap, L)
+        assert np.array_equal(flat_rows[so[ok]], gz[tok[ok]]), f"src {s}: pool payload != z rows"
+        rp = reps[s]
+        assert rp["send_demand"] == list(d["demand"]) and rp["send_count"] == list(d["send_count"])
+        assert rp["send_dropped"] == d["send_dropped"] and rp["send_kept"] == d["send_count"].sum()
+    waves = O.wave_experts(X, W)
+    ret = lay.ret.float().cpu().numpy().astype(np.float64) if act == "bf16" else lay.ret.cpu().numpy()
+    for r in range(R):
+        rv = ref["recv"][r]
+        for w, experts in enumerate(waves):
+            gsrc = host(lay.row_src[r, w])
+            gcnt = host(lay.wave_count[r, w])
+            assert np.array_equal(gcnt, rv["count"][experts]), f"rank {r} wave {w}: counts"
+            assert np.array_equal(gsrc, rv["row_src"][experts]), f"rank {r} wave {w}: row_src"
+        rp = reps[r]
+        assert rp["expert_arrivals"] == list(rv["arrivals"]) and rp["expert_kept"] == list(rv["count"])
+        assert rp["recv_dropped"] == rv["recv_dropped"].sum() and rp["recv_bad_ids"] == 0
+        defined = rv["row_expert"] >= 0
+        dropped = defined & (rv["row_rank"] >= rcap)
+        assert np.all(ret[r][dropped] == 0), f"rank {r}: receive-dropped rows are not zero"
+        assert_stored_close(ret[r][defined], ref["ret"][r][defined], act, f"rank {r} returned rows")
+    led = ref["ledger"]
+    assert sum(rp["recv_kept"] for rp in reps) == led["kept"]
+    assert sum(rp["send_dropped"] for rp in reps) == led["send_dropped"].sum()
+    assert sum(rp["recv_dropped"] for rp in reps) == led["recv_dropped"].sum()
+    for s in range(R):
+        assert_bar(host(lay.out[s]), ref["out"][s]["out_exact"], act, f"src {s} out")
+
+
+@pytest.mark.parametrize("tokens", [0, 1, 65])
+def test_all_ranks_ragged_and_empty(runner, tokens):
+    sh = configs.with_tokens(configs.get("mini_bf16"), tokens)
+    _say(f"[all-ranks] mini_bf16 tokens={tokens}")
+    inp = gen.generate(sh, seed=5, grid=True)
+    ref = O.layer_all_ranks(sh, inp)
+    lay = runner.AllRanksLayer(sh, inp)
+    lay.run()
+    torch.cuda.synchronize()
+    if tokens == 0:
+        ids, _ = _decode_pools(lay.pools, sh.latent, sh.act)
+        assert np.all(ids == -1)
+        for rp in lay.drop_reports():
+            assert rp["send_kept"] == 0 and rp["recv_arrivals"] == 0
+        return
+    _check_all_ranks(sh, inp, ref, lay, True)
+
+
+def test_all_logits_equal_degenerate_router(runner):
+    """W_r = 0: every token picks experts 0..k-1 with weight 1/k; most assignments drop."""
+    sh = configs.get("mini_bf16")
+    _say("[all-ranks] mini_bf16 zero router")
+    inp = gen.generate(sh, seed=6, grid=True)
+    inp["w_router"] = np.zeros_like(inp["w_router"])
+    ref = O.layer_all_ranks(sh, inp)
+    assert ref["ledger"]["send_dropped"].sum() > 0
+    lay = runner.AllRanksLayer(sh, inp)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, True)
+    assert np.all(host(lay.w) == np.float32(1.0 / sh.top_k))
+
+
+def test_deterministic_bitwise(runner):
+    sh = configs.get("mini_bf16_skew")
+    inp = gen.generate(sh, seed=3)
+    outs = []
+    for _ in range(2):
+        lay = runner.AllRanksLayer(sh, inp)
+        lay.run()
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (lay.out, lay.ret, lay.slot_of, lay.row_src, lay.pools)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+# ------------------------------------------------------------ full size
+
+
+def _oracle_token_out(sh, inp, ref, tokens):
+    """Oracle layer output (unrounded) for a few of the receiver's own tokens."""
+    r, X, H, HS, act = inp["receiver"], sh.local_experts, sh.expert_hidden, sh.shared_hidden, sh.act
+    d, rv = ref["dispatch"], ref["recv"]
+    scap, rcap = ref["send_cap"], ref["recv_cap"]
+    xs = inp["x"][tokens]
+    z = O.down_project(xs, inp["w_down"], act)
+    fret = inp["foreign_ret"]
+    c = np.zeros((len(tokens), sh.latent))
+    for a, t in enumerate(tokens):
+        for i in range(sh.top_k):
+            sl = d["slot_of"][t, i]
+            if sl < 0:
+                continue
+            dest, slot = divmod(int(sl), scap)
+            if dest == r:
+                j = int(d["idx"][t, i]) - X * r
+                if rv["row_rank"][r, slot] < rcap:
+                    y = O.expert_ffn(z[a:a + 1], inp["w13"][j], inp["w2"][j], H, act)[0]
+                else:
+                    y = np.zeros(sh.latent)
+            else:
+                y = gen.to_f32(fret[dest, slot]).astype(np.float64)
+            c[a] += float(d["w"][t, i]) * y
+    c = O.round_act(c, act)
+    hs = O.shared_hidden(xs, inp["ws13"], HS, act)
+    _, exact = O.layer_output(c, hs, inp["w_up"], inp["ws2"], act)
+    return z, exact
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_one_rank_full_size(runner, cfg):
+    sh = configs.get(cfg)
+    scap, rcap = O.capacities(sh)
+    _say(f"[full-size] config {cfg} grid=True gather=fused")
+    inp = gen.generate(sh, seed=0, grid=True, send_cap=scap)
+    lay = runner.OneRankLayer(sh, inp, gather="fused")
+    lay.run()
+    torch.cuda.synchronize()
+    rep = lay.drop_report()
+    ref = O.layer_one_rank(sh, inp, with_floats=False)
+    d, rv, r = ref["dispatch"], ref["recv"], inp["receiver"]
+    act, L, X, W = sh.act, sh.latent, sh.local_experts, sh.waves
+    _check_routing(sh, d, host(lay.logits), host(lay.idx), host(lay.w), True, f"cfg{cfg}")
+    assert np.array_equal(host(lay.slot_of), d["slot_of"])
+    assert np.array_equal(host(lay.send_count), d["send_count"])
+    assert rep["send_dropped"] == d["send_dropped"] and rep["send_demand"] == list(d["demand"])
+    ids, rows = _decode_pools(lay.send_pools, L, act)
+    assert np.array_equal(ids, d["pool_ids"])
+    # receive side: exact ranks, counts, drops
+    waves = O.wave_experts(X, W)
+    for w, experts in enumerate(waves):
+        assert np.array_equal(host(lay.wave_count[w]), rv["count"][experts])
+        assert np.array_equal(host(lay.row_src[w]), rv["row_src"][experts])
+    assert rep["expert_arrivals"] == list(rv["arrivals"]) and rep["expert_kept"] == list(rv["count"])
+    assert rep["recv_dropped"] == rv["recv_dropped"].sum() and rep["recv_bad_ids"] == 0
+    if cfg == 4:
+        assert rep["send_dropped"] > 0 and rep["recv_dropped"] > 0
+    # sampled float checks
+    rng = np.random.default_rng(cfg)
+    tokens = np.unique(np.concatenate([[0, sh.tokens - 1], rng.choice(sh.tokens, 30, replace=False)]))
+    z_ref = O.down_project(inp["x"][tokens], inp["w_down"], act)
+    gz = host(lay.z[torch.as_tensor(tokens, device=lay.z.device)])
+    assert np.array_equal(gz, z_ref), "z differs on the grid"
+    so = d["slot_of"][tokens]
+    for a in range(len(tokens)):
+        for i in range(sh.top_k):
+            if so[a, i] >= 0:
+                dest, slot = divmod(int(so[a, i]), scap)
+                assert np.array_equal(rows[dest, slot], z_ref[a])
+    if sh.layer != "full":
+        return
+    # returned rows of sampled received rows (from other sources)
+    ret = host(lay.ret_send)
+    frows = inp["foreign_rows"]
+    for w, experts in enumerate(waves):
+        for jw, j in enumerate(experts):
+            n = rv["count"][j]
+            for q in rng.choice(n, min(n, 24), replace=False):
+                src, slot = divmod(int(rv["row_src"][j, q]), scap)
+                if src == r:
+                    continue
+                y = O.expert_ffn(gen.to_f32(frows[src, slot:slot + 1]).astype(np.float64), inp["w13"][j],
+                                 inp["w2"][j], sh.expert_hidden, act)[0]
+                assert_stored_close(ret[src, slot], y, act, f"returned row ({src},{slot}) expert {j}")
+    # layer output for sampled own tokens
+    _, out_exact = _oracle_token_out(sh, inp, ref, tokens)
+    gout = host(lay.out[torch.as_tensor(tokens, device=lay.out.device)])
+    ratio, raw = assert_bar(gout, out_exact, act, f"cfg{cfg} out (sampled tokens)")
+    _say(f"[full-size] config {cfg}: bar ratio {ratio:.3g}, raw max|d|/rms {raw:.3g}")
