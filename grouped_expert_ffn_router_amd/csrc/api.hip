@@ -66,8 +66,9 @@ int derive(const moe_dims* d, Q* q) {
   if (bf16) {
     if (d->d_model % 64 || d->latent % 64 || d->expert_hidden % 64 || d->shared_hidden % 64)
       return fail(MOE_EINVAL, "bf16 layers need d_model, latent, expert_hidden, shared_hidden multiples of 64");
-  } else if (d->latent % 8) {
-    return fail(MOE_EINVAL, "fp32 layers need latent to be a multiple of 8");
+  } else if (d->latent % 8 || d->shared_hidden % 4) {
+    // the combined [latent | shared hidden] rows are written with 16-byte stores
+    return fail(MOE_EINVAL, "fp32 layers need latent a multiple of 8 and shared_hidden a multiple of 4");
   }
   q->T = d->tokens; q->D = d->d_model; q->L = d->latent; q->E = d->n_experts; q->k = d->top_k;
   q->R = d->n_ranks; q->X = X; q->W = d->waves; q->WX = X / d->waves; q->H = d->expert_hidden;

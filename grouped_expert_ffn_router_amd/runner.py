@@ -22,13 +22,13 @@ from . import binding as B
 
 
 def upload(arr, device):
-    """Host storage array (uint16 bf16 bit patterns or float32) -> device tensor."""
+    """Host array (uint16 bf16 bit patterns, float32, int32 or raw bytes) -> device tensor."""
     a = np.ascontiguousarray(arr)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
     if a.dtype == np.float32:
         return torch.from_numpy(a).to(device)
-    if a.dtype == np.int32:
+    if a.dtype in (np.int32, np.uint8):
         return torch.from_numpy(a).to(device)
     raise TypeError(f"unsupported host dtype {a.dtype}")
 

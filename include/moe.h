@@ -32,7 +32,8 @@
  *     thread-local message for the last failure.  No exception crosses the
  *     ABI.  Identical inputs give bit-identical outputs (no atomics).
  *   - bf16 layers need d_model, latent, expert_hidden and shared_hidden to be
- *     multiples of 64; fp32 layers need latent to be a multiple of 8.
+ *     multiples of 64; fp32 layers need latent a multiple of 8 and
+ *     shared_hidden a multiple of 4.
  */
 #ifndef MOE_H
 #define MOE_H

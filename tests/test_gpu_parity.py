@@ -165,6 +165,9 @@ def test_all_logits_equal_degenerate_router(runner):
 
 
 def test_deterministic_bitwise(runner):
+    """Two runs give bit-identical results (no atomics, fixed reduction orders).
+    Pool bytes are compared where the layer defines them: every id, and the
+    payload of filled rows (an empty row's payload is left unwritten)."""
     sh = configs.get("mini_bf16_skew")
     inp = gen.generate(sh, seed=3)
     outs = []
@@ -172,10 +175,12 @@ def test_deterministic_bitwise(runner):
         lay = runner.AllRanksLayer(sh, inp)
         lay.run()
         torch.cuda.synchronize()
-        outs.append([t.clone() for t in (lay.out, lay.ret, lay.slot_of, lay.row_src, lay.pools)])
+        ids, rows = _decode_pools(lay.pools, sh.latent, sh.act)
+        rows[ids < 0] = 0
+        outs.append([host(t) for t in (lay.out, lay.ret, lay.slot_of, lay.row_src, lay.wave_count, lay.w,
+                                       lay.logits, lay.z)] + [ids, rows])
     for a, b in zip(*outs):
-        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
-                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+        assert a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 # ------------------------------------------------------------ full size
