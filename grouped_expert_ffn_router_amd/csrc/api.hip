@@ -66,6 +66,7 @@ int derive(const moe_dims* d, Q* q) {
   if (bf16) {
     if (d->d_model % 64 || d->latent % 64 || d->expert_hidden % 64 || d->shared_hidden % 64)
       return fail(MOE_EINVAL, "bf16 layers need d_model, latent, expert_hidden, shared_hidden multiples of 64");
+    if (d->n_experts % 4) return fail(MOE_EINVAL, "bf16 layers need n_experts to be a multiple of 4");
   } else if (d->latent % 8 || d->shared_hidden % 4) {
     // the combined [latent | shared hidden] rows are written with 16-byte stores
     return fail(MOE_EINVAL, "fp32 layers need latent a multiple of 8 and shared_hidden a multiple of 4");
@@ -148,18 +149,12 @@ P* at(void* ws, size_t off) { return (P*)((char*)ws + off); }
 
 template <bool GATEUP, class A, class B, class E>
 hipError_t gemm_bf16(A a, B b, E e, int N, int K, int64_t max_rows, int groups, hipStream_t st) {
-  constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
-  using TL = MfmaTile<BM, BN, WM, WN>;
+  using Cfg = TileCfg<256, 256>;
   if (N <= 0 || max_rows <= 0 || groups <= 0) return hipSuccess;
-  auto kern = gemm_bf16_mfma<BM, BN, WM, WN, GATEUP, A, B, E>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t r = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::LDS_BYTES);
-    if (r != hipSuccess) return r;
-    attr = true;
-  }
-  const dim3 grid((unsigned)ceil_div(N, BN), (unsigned)ceil_div(max_rows, BM), (unsigned)groups);
-  hipLaunchKernelGGL(kern, grid, dim3(TL::NT), TL::LDS_BYTES, st, a, b, e, N, K);
+  const int64_t tiles_m = ceil_div(max_rows, Cfg::BM), tiles_n = ceil_div(N, Cfg::BN);
+  const int64_t nb = groups * tiles_m * tiles_n;
+  hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, GATEUP, A, B, E>), dim3((unsigned)nb), dim3(Cfg::NT), 0, st, a, b, e, N,
+                     K, (int)tiles_m, (int)tiles_n);
   return hipGetLastError();
 }
 
@@ -266,7 +261,8 @@ int moe_route(const moe_dims* dims, const void* x, const void* w_router, const v
   if (q.T == 0) return MOE_OK;
   NEED(x, "x"); NEED(w_router, "w_router"); NEED(w_down, "w_down"); NEED(z, "z");
   NEED4(topk_idx, "topk_idx"); NEED4(topk_w, "topk_w"); NEED(ws, "ws");
-  if (logits && ((uintptr_t)logits & 3)) return fail(MOE_EALIGN, "logits is not 4-byte aligned");
+  if (logits && !aligned16(logits)) return fail(MOE_EALIGN, "logits is not 16-byte aligned");
+  if (bias && !aligned16(bias)) return fail(MOE_EALIGN, "bias is not 16-byte aligned");
   if (bias_row_tokens < 0) return fail(MOE_EINVAL, "bias_row_tokens < 0");
   const WsLayout w = layout(q);
   hipStream_t st = (hipStream_t)stream;

@@ -4,8 +4,21 @@
 // grouped expert FFNs (row gather from the receive pools, SwiGLU pairing,
 // scatter into the return pools) and the shared experts + up-projection.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 tiles (gfx950), LDS double buffering
-// with a padded row pitch (conflict-free 16-byte fragment reads).
+// bf16 path (gfx950): one 256-thread workgroup (4 waves, 2 x 2) per BM x BN
+// output tile; each wave owns a (BM/2) x (BN/2) sub-tile built from
+// v_mfma_f32_32x32x16_bf16.  K advances in steps of 64: the next step's
+// operands go straight from HBM into the second LDS buffer (direct 16-byte
+// global->LDS loads, each group of 8 lanes reading one full 128-byte row
+// segment) while the current step's MFMAs run.  LDS rows are 128 bytes
+// with the 16-byte chunk index XOR-swizzled per row, so the fragment reads
+// of any 8 (or 16) consecutive lanes touch every LDS bank once.
+// The MFMA is issued with the B fragment as its first operand, so every lane
+// ends up holding one output row m and runs of 4 consecutive columns n: the
+// epilogue stores 8-byte pieces and resolves a row's destination once.
+// Workgroup ids are remapped so that each XCD (blocks are dealt round-robin
+// to the 8 XCDs) works on a contiguous, M-grouped range of tiles and reuses
+// operand rows from its own L2.
+//
 // fp32 path: a plain per-element kernel (small layers only).
 #pragma once
 
@@ -44,7 +57,8 @@ struct AGather {  // row m of group g = payload of receive-pool row row_src[g][m
 
 // ------------------------------------------------------------ B operands
 // ptr(g, n, k): address of B[n][k] for group g.  KSEG: the row pointer
-// depends on k (re-evaluated every K tile); otherwise it is hoisted.
+// depends on k (re-evaluated every K step, which never straddles a segment);
+// otherwise it is computed once.
 
 template <class T>
 struct BRows {  // row n of group g at base + g*group_stride + n*ldb
@@ -107,6 +121,29 @@ struct BKSeg {
 };
 
 // ------------------------------------------------------------ epilogues
+// Scalar interface (fp32 kernel): store(g, m, n, v) / store2(g, m, u, gate, up).
+// Vector interface (MFMA kernel): row(g, m) -> per-row context, then
+// store4(ctx, n, v[4]) for columns n..n+3 (n % 4 == 0, clipped at N), or
+// store4_pair(ctx, u, gate[4], up[4]) for hidden units u..u+3.
+
+__device__ __forceinline__ uint2 pack_bf16x4(const float* v) {
+  return make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                    (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+}
+
+// 4 consecutive activations at p (8-byte aligned for bf16 when full).
+template <class T>
+__device__ __forceinline__ void put4(T* p, const float* v, int valid) {
+  if constexpr (sizeof(T) == 2) {
+    if (valid >= 4) {
+      *(uint2*)p = pack_bf16x4(v);
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)  // fixed trip count: v stays in registers
+    if (i < valid) p[i] = Act<T>::store(v[i]);
+}
 
 template <class T>
 struct ERouteDown {  // columns < E: fp32 logits (+bias); the rest: latent z
@@ -123,6 +160,26 @@ struct ERouteDown {  // columns < E: fp32 logits (+bias); the rest: latent z
       z[(int64_t)m * L + (n - E)] = Act<T>::store(v);
     }
   }
+  // Vector interface: needs E % 4 == 0, so a group of 4 columns is either
+  // all logits or all latent.
+  struct Row {
+    float* lg;
+    T* zr;
+    const float* b;
+  };
+  __device__ Row row(int, int m) const {
+    return {logits + (int64_t)m * E, z + (int64_t)m * L,
+            bias ? bias + (int64_t)(bias_row_tokens ? m / bias_row_tokens : 0) * E : nullptr};
+  }
+  __device__ void store4(const Row& r, int n, int N, const float* v) const {
+    if (n < E) {
+      float b[4] = {0.f, 0.f, 0.f, 0.f};
+      if (r.b) *(float4*)b = *(const float4*)(r.b + n);
+      *(float4*)(r.lg + n) = make_float4(v[0] + b[0], v[1] + b[1], v[2] + b[2], v[3] + b[3]);
+    } else {
+      put4(r.zr + (n - E), v, N - n);
+    }
+  }
 };
 
 template <class T>
@@ -133,6 +190,14 @@ struct ESwiGLU {  // hidden unit u of row m: act(silu(gate) * up)
   __device__ void store2(int g, int m, int u, float gate, float up) const {
     out[g * group_stride + (int64_t)m * ldo + col0 + u] = Act<T>::store(silu(gate) * up);
   }
+  struct Row { T* p; };
+  __device__ Row row(int g, int m) const { return {out + g * group_stride + (int64_t)m * ldo + col0}; }
+  __device__ void store4_pair(const Row& r, int u, const float* gate, const float* up) const {
+    float h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = silu(gate[i]) * up[i];
+    put4(r.p + u, h, 4);
+  }
 };
 
 template <class T>
@@ -142,11 +207,15 @@ struct EScatter {  // row m of group g -> return row of receive row row_src[g][m
   int cap;
   const int32_t* row_src;
   int64_t rs_stride;
-  __device__ void store(int g, int m, int n, float v) const {
+  __device__ T* dest(int g, int m) const {
     const int rs = row_src[g * rs_stride + m];
     const int s = rs / cap, sl = rs - s * cap;
-    ((T*)(ret + s * src_stride + (int64_t)sl * row_bytes))[n] = Act<T>::store(v);
+    return (T*)(ret + s * src_stride + (int64_t)sl * row_bytes);
   }
+  __device__ void store(int g, int m, int n, float v) const { dest(g, m)[n] = Act<T>::store(v); }
+  struct Row { T* p; };
+  __device__ Row row(int g, int m) const { return {dest(g, m)}; }
+  __device__ void store4(const Row& r, int n, int N, const float* v) const { put4(r.p + n, v, N - n); }
 };
 
 template <class T>
@@ -154,75 +223,131 @@ struct EStore {
   T* out;
   int64_t ldo;
   __device__ void store(int, int m, int n, float v) const { out[(int64_t)m * ldo + n] = Act<T>::store(v); }
+  struct Row { T* p; };
+  __device__ Row row(int, int m) const { return {out + (int64_t)m * ldo}; }
+  __device__ void store4(const Row& r, int n, int N, const float* v) const { put4(r.p + n, v, N - n); }
 };
 
 // ------------------------------------------------------------ bf16 MFMA kernel
 
-template <int BM, int BN, int WM, int WN>
-struct MfmaTile {
-  static constexpr int NT = 64 * WM * WN;
-  static constexpr int BK = 64;
-  static constexpr int PITCH = BK + 8;  // elements; 144-byte rows
-  static constexpr int LDS_BYTES = 2 * (BM + BN) * PITCH * 2;
+template <int BM_, int BN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int NT = 256;                          // 4 waves, 2 x 2
+  static constexpr int WTM = BM / 2, WTN = BN / 2;        // wave sub-tile
+  static constexpr int FM = WTM / 32, FN = WTN / 32;      // 32x32 fragments per wave
+  static constexpr int LA = BM / 32, LB = BN / 32;        // 16-byte loads per lane per K step
+  static constexpr int STAGE = (BM + BN) * 128;           // bytes of one LDS buffer
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sides are multiples of 64");
 };
 
-// grid: (ceil(N/BN), ceil(max_rows/BM), groups); block: 64*WM*WN threads.
-// K must be a multiple of 64.  GATEUP: N counts gate+up columns (blocks of
-// 64) and the epilogue gets (gate, up) pairs; WN*64 must divide BN.
-template <int BM, int BN, int WM, int WN, bool GATEUP, class A, class B, class E>
-__global__ void __launch_bounds__(64 * WM * WN)
-gemm_bf16_mfma(A a, B b, E e, int N, int K) {
-  using TL = MfmaTile<BM, BN, WM, WN>;
-  constexpr int NT = TL::NT, BK = TL::BK, PITCH = TL::PITCH;
-  constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
-  constexpr int CA = BM * BK / 8 / NT, CB = BN * BK / 8 / NT;
-  static_assert(CA * NT * 8 == BM * BK && CB * NT * 8 == BN * BK, "tile/threads mismatch");
-  static_assert(!GATEUP || (WTN % 64) == 0, "gate/up pairs need 64-column wave tiles");
-  extern __shared__ __attribute__((aligned(16))) bf16_t sm[];
+// Logical tile of workgroup `bid`: XCD-contiguous ranges, M-grouped order
+// inside a group.  Returns false past the end.
+__device__ __forceinline__ void tile_of(int bid, int nb, int tiles_m, int tiles_n, int& g, int& tm, int& tn) {
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  const int logical = xcd * per + min(xcd, rem) + idx;
+  const int tpg = tiles_m * tiles_n;
+  g = logical / tpg;
+  const int r = logical - g * tpg;
+  constexpr int GROUP_M = 8;
+  const int width = GROUP_M * tiles_n;
+  const int gid = r / width, first_m = gid * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int rr = r - gid * width;
+  tm = first_m + rr % gsz;
+  tn = rr / gsz;
+}
 
-  const int g = blockIdx.z;
+// 16-byte LDS read at byte address `addr`, issued as inline assembly: the
+// result must be awaited with lgkm_wait before use.
+__device__ __forceinline__ void lds_read16(bf16x8& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+}
+
+// Wait until at most N LDS reads are outstanding; the fragments pass through
+// the statement so that their consumers stay behind it.
+template <int N, int FM, int FN>
+__device__ __forceinline__ void lgkm_wait(bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
+  static_assert(FM == 4 && FN == 4, "fragment counts of the 256 x 256 tile");
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]),
+                 "+v"(fb[3])
+               : "i"(N)
+               : "memory");
+}
+
+// 16-byte chunk swizzle of a 128-byte LDS row.  Rows r and r' with the same
+// swizzle never share a 16-lane (64-bank) or an 8-lane (32-bank) read group:
+// f(r) = (r >> 1) ^ 4 (r & 1) is a permutation of 0..7 over any 8 consecutive
+// rows and over any 8 rows of one parity among 16 consecutive rows.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
+
+// grid: (groups * tiles_m * tiles_n); block: 256.  K must be a multiple of 64.
+// GATEUP: N counts gate+up columns (blocks of 64) and the epilogue gets
+// (gate, up) pairs.
+//
+// One K step (64) of the main loop: wait for this step's tiles to land in LDS
+// and pass the barrier; issue every fragment read of the step; then issue the
+// direct HBM->LDS loads of the next step into the other buffer (nobody reads
+// that buffer any more: all its fragment reads were consumed before the
+// barrier); then run the step's MFMAs while those loads are in flight.
+// Issuing the loads after the reads keeps them off the reads' dependence
+// path, and no staging registers are needed.
+template <class Cfg, bool GATEUP, class A, class B, class E>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WTM = Cfg::WTM, WTN = Cfg::WTN;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, LA = Cfg::LA, LB = Cfg::LB, STAGE = Cfg::STAGE;
+  constexpr int KS = BK / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  int g, tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, g, tm, tn);
   const int M = a.rows(g);
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int m0 = tm * BM, n0 = tn * BN;
   if (m0 >= M) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave >> 1, wn = wave & 1;
 
-  const bf16_t* arow[CA];
-  int a_sm[CA];
+  // Loader: load slot i of a wave fills the 1 KB LDS block i*4 + wave, i.e.
+  // rows r = (i*4 + wave)*8 + lane/8, lane landing at block + 16*lane.  That
+  // LDS position holds swizzled chunk lane%8 of row r, so the lane fetches
+  // global chunk (lane%8) ^ swz(r); all rows of a lane are 32 apart and share
+  // the swizzle.
+  const int lrow = lane >> 3, lcol = lane & 7;
+  const int r0 = wave * 8 + lrow;
+  const int gcol = (lcol ^ swz(r0)) * 8;
+  const bf16_t* pa[LA];
 #pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int c = tid + i * NT, r = c >> 3, kc = (c & 7) * 8;
-    arow[i] = a.row(g, min(m0 + r, M - 1)) + kc;
-    a_sm[i] = r * PITCH + kc;
+  for (int i = 0; i < LA; ++i) pa[i] = a.row(g, min(m0 + r0 + 32 * i, M - 1)) + gcol;
+  const bf16_t* pb[LB];
+  int nb_row[LB];
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    nb_row[i] = min(n0 + r0 + 32 * i, N - 1);
+    pb[i] = b.ptr(g, nb_row[i], gcol);
   }
-  const bf16_t* brow[CB];
-  int bn[CB], bkc[CB], b_sm[CB];
+  auto dma = [&](int st, int k0) {
+    char* s = smem + st * STAGE + wave * 1024;
 #pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int c = tid + i * NT, r = c >> 3, kc = (c & 7) * 8;
-    bn[i] = min(n0 + r, N - 1);
-    bkc[i] = kc;
-    brow[i] = b.ptr(g, bn[i], kc);
-    b_sm[i] = (BM + r) * PITCH + kc;
-  }
-
-  uint4 ra[CA], rb[CB];
-  auto gload = [&](int k0) {
+    for (int i = 0; i < LA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(pa[i] + k0), (__attribute__((address_space(3))) void*)(s + i * 4096),
+                                       16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < CA; ++i) ra[i] = *(const uint4*)(arow[i] + k0);
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const bf16_t* p = B::KSEG ? b.ptr(g, bn[i], k0 + bkc[i]) : brow[i] + k0;
-      rb[i] = *(const uint4*)p;
+    for (int i = 0; i < LB; ++i) {
+      const bf16_t* p = B::KSEG ? b.ptr(g, nb_row[i], k0 + gcol) : pb[i] + k0;
+      __builtin_amdgcn_global_load_lds((const void*)p,
+                                       (__attribute__((address_space(3))) void*)(s + BM * 128 + i * 4096), 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-    bf16_t* s = sm + buf * (BM + BN) * PITCH;
-#pragma unroll
-    for (int i = 0; i < CA; ++i) *(uint4*)(s + a_sm[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < CB; ++i) *(uint4*)(s + b_sm[i]) = rb[i];
-  };
+
+  // Fragment reads: lane reads row (base + lane%32), 16-byte chunk ks*2 + lane/32.
+  // Fragment rows are 32 apart, so one swizzle serves them all.
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int fswz = swz(frow);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const uint32_t fa_base = lds0 + (wm * WTM + frow) * 128, fb_base = lds0 + BM * 128 + (wn * WTN + frow) * 128;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -232,53 +357,89 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const bf16_t* s = sm + buf * (BM + BN) * PITCH;
+  // The fragment reads are issued as inline ds_read_b128 so that the
+  // compiler, which cannot tell the two LDS buffers apart, does not make
+  // them wait for the in-flight HBM->LDS loads of the other buffer; their
+  // completion is awaited explicitly (lgkm_wait ties the fragments, so no
+  // MFMA can be scheduled before the wait that covers its operands).
+  bf16x8 fa[KS][FM], fb[KS][FN];
+  auto read_step = [&](uint32_t st_off, int ks) {
+    const uint32_t ch = (uint32_t)(((ks * 2 + fhalf) ^ fswz) << 4) + st_off;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[FM], bfv[FN];
+    for (int i = 0; i < FM; ++i) lds_read16(fa[ks][i], fa_base + ch + i * 4096);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *(const bf16x8*)(s + (wm * WTM + i * 32 + frag_row) * PITCH + ks * 16 + frag_k);
+    for (int j = 0; j < FN; ++j) lds_read16(fb[ks][j], fb_base + ch + j * 4096);
+  };
+  auto mma_step = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfv[j] = *(const bf16x8*)(s + (BM + wn * WTN + j * 32 + frag_row) * PITCH + ks * 16 + frag_k);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+  };
 
-  // 32x32 accumulator layout: lane l holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4.
-  const int col_l = lane & 31, row_l = (lane >> 5) * 4;
+  const int nk = K / BK;
+  dma(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // next step's tiles go to the other buffer, whose last reads completed
+    // before the barrier; the last step re-fetches its own slice there
+    dma((kt + 1) & 1, min(kt + 1, nk - 1) * BK);
+    const uint32_t st_off = (kt & 1) * STAGE;
+    read_step(st_off, 0);
+    read_step(st_off, 1);
+    lgkm_wait<FM + FN>(fa[0], fb[0]);
+    mma_step(0);
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
+        read_step(st_off, ks + 1);
+        lgkm_wait<FM + FN>(fa[ks], fb[ks]);
+      } else {
+        lgkm_wait<0>(fa[ks], fb[ks]);
+      }
+      mma_step(ks);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write outlives the loop
+
+  // Accumulator layout (B fragment first): lane holds row m = base + lane%32 and
+  // columns n = base + 8*(v/4) + 4*(lane/32) + v%4.
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + frow;
+    if (m >= M) continue;
+    const auto rc = e.row(g, m);
+    if constexpr (GATEUP) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * WTM + i * 32 + (v >> 2) * 8 + row_l + (v & 3);
-      if (m >= M) continue;
-      if constexpr (GATEUP) {
+      for (int j = 0; j < FN; j += 2) {
 #pragma unroll
-        for (int j = 0; j < FN; j += 2) {
-          const int n = n0 + wn * WTN + j * 32 + col_l;  // gate column
-          if (n < N) e.store2(g, m, (n >> 6) * 32 + (n & 31), acc[i][j][v], acc[i][j + 1][v]);
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * WTN + j * 32 + q * 8 + fhalf * 4;  // gate column (n % 64 < 32)
+          if (n < N) {
+            float gv[4], uv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              gv[t] = acc[i][j][q * 4 + t];
+              uv[t] = acc[i][j + 1][q * 4 + t];
+            }
+            e.store4_pair(rc, (n >> 6) * 32 + (n & 31), gv, uv);
+          }
         }
-      } else {
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int n = n0 + wn * WTN + j * 32 + col_l;
-          if (n < N) e.store(g, m, n, acc[i][j][v]);
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * WTN + j * 32 + q * 8 + fhalf * 4;
+          if (n < N) {
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = acc[i][j][q * 4 + t];
+            e.store4(rc, n, N, v);
+          }
         }
       }
     }

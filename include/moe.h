@@ -16,8 +16,8 @@
  *
  * Conventions (all entry points):
  *   - Every data pointer is a DEVICE pointer owned by the caller.  Activation,
- *     weight, pool and workspace buffers are 16-byte aligned; int32 / fp32
- *     index, weight and count arrays 4-byte aligned.  A buffer of zero
+ *     weight, pool, workspace, logit and bias buffers are 16-byte aligned;
+ *     int32 / fp32 index, routing-weight and count arrays 4-byte aligned.  A buffer of zero
  *     elements may be NULL.  The library never allocates or frees caller
  *     memory.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
@@ -32,8 +32,8 @@
  *     thread-local message for the last failure.  No exception crosses the
  *     ABI.  Identical inputs give bit-identical outputs (no atomics).
  *   - bf16 layers need d_model, latent, expert_hidden and shared_hidden to be
- *     multiples of 64; fp32 layers need latent a multiple of 8 and
- *     shared_hidden a multiple of 4.
+ *     multiples of 64 and n_experts a multiple of 4; fp32 layers need latent
+ *     a multiple of 8 and shared_hidden a multiple of 4.
  */
 #ifndef MOE_H
 #define MOE_H
