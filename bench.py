@@ -1,16 +1,29 @@
 """Benchmark of one EP rank's fixed-pool, three-wave MoE layer on one MI355X.
 
-One step = the whole layer for one batch: route -> pack into 64 fixed send
+One step = the whole layer for one batch of the rank's tokens: route (router
++ latent down-projection GEMM, top-k select) -> pack into the 64 fixed send
 pools -> (self-block of the dispatch exchange) -> 3 waves of receive + expert
-SwiGLU GEMMs -> (self-block of the return exchange) -> combine + up-projection
-+ shared experts.  Inputs are resident in HBM before timing starts.  The
-metric is routed token-assignments per second: T * k / step time.
+SwiGLU GEMMs (rows scattered into the return pools) -> (self-block of the
+return exchange) -> weighted combine + up-projection + shared experts.  The
+pools the other 63 ranks send, and the rows they return, are seeded inputs
+resident in HBM before timing starts.  The metric is routed
+token-assignments per second: T * k / step time.
 
-Prints ONE JSON line.  Options: --steps K --warmup W --config {2,3,4,5}
---gather {fused,buffer} --no-cpu-baseline --cpu-tokens N.
+Prints ONE JSON line with, besides the contract fields:
+  roofline      the dominant kernel (largest summed time) against its peak,
+                timed live with HIP events on the stream it runs on
+                (moe_timing_*), with HBM traffic from the committed rocprofv3
+                counter summary when that summary matches the current sources
+  kernels       every kernel's average duration and roofline fraction
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same layer
+
+Options: --steps K --warmup W --config {2,3,4,5} --gather {fused,buffer}
+--no-cpu-baseline --cpu-tokens N --seed S.  --gpus N > 1 exits: this build
+measures one GPU.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -18,9 +31,16 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
 METRIC = "routed token-assignments/s per GPU (dispatch+expert+combine); HBM GB/s, MFMA %"
-PEAK_MFMA_BF16_TFLOPS = 2500.0
-PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+SOURCES = ["grouped_expert_ffn_router_amd/csrc/api.hip", "grouped_expert_ffn_router_amd/csrc/kernels.hip",
+           "grouped_expert_ffn_router_amd/csrc/gemm.h", "grouped_expert_ffn_router_amd/csrc/moe_common.h",
+           "grouped_expert_ffn_router_amd/csrc/moe_internal.h"]
 
 
 def parse():
@@ -32,15 +52,71 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--gather", choices=["fused", "buffer"], default="fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens per rank of the CPU-oracle sample (0: the whole workload)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
 
 
+def source_digest():
+    h = hashlib.sha256()
+    for p in SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/<kernel>_<workload>_pmc.txt, if that
+    summary was taken from the current sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_work(sh, kept_rows_per_wave, send_kept, send_cap):
+    """Algorithmic flops (GEMMs) or bytes (data movement) of one launch of each kernel.
+
+    GEMMs count 2*M*N*K over the rows the layer keeps (never capacity padding);
+    data-movement kernels count the bytes the method must move."""
+    T, D, L, E, k, R = sh.tokens, sh.d_model, sh.latent, sh.n_experts, sh.top_k, sh.n_ranks
+    H, S, HS = sh.expert_hidden, sh.shared_experts, sh.shared_hidden
+    es = 2 if sh.act == "bf16" else 4
+    rows = float(np.mean(kept_rows_per_wave)) if len(kept_rows_per_wave) else 0.0
+    return {
+        "route_gemm": ("flop", 2.0 * T * (E + L) * D),
+        "expert_gate_up": ("flop", 2.0 * rows * 2 * H * L),
+        "expert_down": ("flop", 2.0 * rows * L * H),
+        "shared_gate_up": ("flop", 2.0 * T * 2 * S * HS * D),
+        "up_shared_down": ("flop", 2.0 * T * D * (L + S * HS)),
+        # read z once, write each kept row (payload + id), ids of empty slots,
+        # read top-k ids, write slot_of
+        "pack": ("byte", T * L * es + send_kept * (L * es + 4) + 4.0 * (R * send_cap - send_kept) + 8.0 * T * k),
+        # read every returned row of the rank's kept assignments, the weights
+        # and slots, write c
+        "combine": ("byte", send_kept * L * es + 8.0 * T * k + T * L * es),
+    }
+
+
 def cpu_baseline(cfg, seed, tokens):
-    """Time the CPU oracle on the same workload with fewer tokens per rank."""
+    """Time the CPU oracle on a bounded sample: the same layer at `tokens` tokens per rank."""
     from oracle import moe_oracle as O
     from workload import configs, gen
-    sh = configs.with_tokens(configs.get(cfg), tokens)
+    base = configs.get(cfg)
+    sh = configs.with_tokens(base, tokens) if tokens != base.tokens else base
     scap, _ = O.capacities(sh)
     inp = gen.generate(sh, seed=seed, send_cap=scap)
     threads = os.cpu_count()
@@ -54,16 +130,19 @@ def cpu_baseline(cfg, seed, tokens):
     t0 = time.perf_counter()
     O.layer_one_rank(sh, inp, with_floats=True)
     dt = time.perf_counter() - t0
+    what = "route + pack + receive" if sh.layer != "full" else "the full layer"
+    scope = (f"the whole {base.name} workload" if tokens == base.tokens else
+             f"the {base.name} recipe at {tokens} tokens per rank (send pools of {scap} rows)")
     return {"value": tokens * sh.top_k / dt, "unit": "assignments/s", "cores": threads, "kind": "oracle",
-            "sample": f"{sh.name}: the same layer with {tokens} tokens per rank (send pools {scap} rows), "
-                      f"full float64 oracle, {dt:.2f} s"}
+            "sample": f"{scope}: {what} of one rank in the float64 oracle (seed {seed}), input generation "
+                      f"excluded, one run of {dt:.1f} s"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU: one EP rank's share of the layer at its real "
-                                   "shape; runs on more than one GPU are not part of it", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark measures one GPU: one EP rank's share of the layer at its real "
+                                   "shape; multi-GPU runs are not part of it", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     from workload import configs, gen
@@ -79,78 +158,78 @@ def main():
     stream = torch.cuda.current_stream()
     full = sh.layer == "full"
 
-    def step(ev=None):
-        # events between the C-ABI calls time each call on the stream it runs on
-        def mark(name):
-            if ev is not None:
-                e = torch.cuda.Event(enable_timing=True)
-                e.record(stream)
-                ev.append((name, e))
-        mark("start")
-        lay.dispatch(stream)
-        mark("dispatch")
-        for w in range(sh.waves):
-            lay.receive_wave(w, stream)
-            mark(f"recv{w}")
-            if full:
-                lay.expert_wave(w, stream)
-                mark(f"expert{w}")
-        if full:
-            lay.combine(stream)
-            mark("combine")
-
     for _ in range(args.warmup):
-        step()
+        lay.run(stream)
     torch.cuda.synchronize()
-    # whole-step timing
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(args.steps):
-        step()
+        lay.run(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    # per-call timing (separate pass, events between calls)
-    per = {}
+
+    # per-kernel pass: every library launch bracketed by HIP events on its stream
+    binding.timing_read()
+    binding.timing_enable(True)
     for _ in range(args.steps):
-        ev = []
-        step(ev)
+        lay.run(stream)
+    torch.cuda.synchronize()
+    per = binding.timing_read()
+    binding.timing_enable(False)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
         torch.cuda.synchronize()
-        for (a, ea), (b, eb) in zip(ev[:-1], ev[1:]):
-            key = b if not b[-1].isdigit() else b[:-1]
-            per.setdefault(key, []).append(ea.elapsed_time(eb))
+
     rep = lay.drop_report(stream)
-    T, k, L, H = sh.tokens, sh.top_k, sh.latent, sh.expert_hidden
-    value = T * k / (ms * 1e-3)
-    waves_rows = lay.wave_count.sum(dim=1).cpu().numpy()
-    # per-call average per launch
-    brk = {key: float(np.mean(v)) for key, v in per.items()}
+    T, k = sh.tokens, sh.top_k
+    kept_waves = lay.wave_count.sum(dim=1).cpu().numpy() if full else np.zeros(0)
+    work = algorithmic_work(sh, kept_waves, rep["send_kept"], scap)
+    kernels = {}
+    for name, (n, tot) in per.items():
+        avg = tot / max(n, 1)
+        ent = {"launches_per_step": n / args.steps, "avg_ms": avg}
+        if name in work and avg > 0:
+            kind, amount = work[name]
+            if kind == "flop":
+                ach = amount / (avg * 1e-3) / 1e12
+                ent.update(unit="TFLOP/s", achieved=ach, frac=ach / PEAK_MFMA_BF16_TFLOPS)
+            else:
+                ach = amount / (avg * 1e-3) / 1e9
+                ent.update(unit="GB/s", achieved=ach, frac=ach / PEAK_HBM_GBS)
+        kernels[name] = ent
+    dom = max(per, key=lambda n: per[n][1])
+    d = kernels[dom]
+    kind = work[dom][0] if dom in work else None
     out = {
-        "metric": METRIC, "value": value, "unit": "assignments/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": sh.act, "data": "synthetic",
-        "config": {"workload": sh.name, "tokens_per_rank": T, "d_model": sh.d_model, "latent": L,
+        "metric": METRIC, "value": T * k / (ms * 1e-3), "unit": "assignments/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if sh.act == "bf16" else "f32",
+        "data": "synthetic (seeded; shapes of the pages' 4K-context expert layer)",
+        "config": {"workload": sh.name, "tokens_per_rank": T, "d_model": sh.d_model, "latent": sh.latent,
                    "experts": sh.n_experts, "top_k": k, "ep_ranks": sh.n_ranks, "local_experts": sh.local_experts,
-                   "waves": sh.waves, "expert_hidden": H, "shared_experts": sh.shared_experts,
-                   "shared_hidden": sh.shared_hidden, "send_cap": scap, "recv_cap": rcap,
-                   "gather": args.gather, "parallelism": "ep64, one rank's share"},
-        "breakdown_ms": brk,
-        "drops": {"send_dropped": rep["send_dropped"], "recv_dropped": rep["recv_dropped"],
-                  "recv_kept": rep["recv_kept"], "send_kept": rep["send_kept"]},
+                   "waves": sh.waves, "expert_hidden": sh.expert_hidden, "shared_experts": sh.shared_experts,
+                   "shared_hidden": sh.shared_hidden, "send_cap": scap, "recv_cap": rcap, "gather": args.gather,
+                   "parallelism": "one EP rank of 64 (the other ranks' pools and returns are inputs)"},
     }
-    if full:
-        # dominant step: the grouped SwiGLU expert GEMMs (moe_expert_gemm), per wave launch
-        rows = float(np.mean(waves_rows))
-        flops = 6.0 * L * H * rows
-        t_ms = brk["expert"]
-        ach = flops / (t_ms * 1e-3) / 1e12
-        out["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / PEAK_MFMA_BF16_TFLOPS, "traffic": None,
-                           "kernel": "moe_expert_gemm (gate/up + down GEMMs of one wave, 2 experts)",
-                           "work_per_launch": f"6*L*H flops x {rows:.0f} kept rows"}
+    if kind is not None:
+        traffic = committed_traffic(dom, sh.name)
+        out["roofline"] = {"bound": "mfma" if kind == "flop" else "hbm", "achieved": d["achieved"],
+                           "peak": PEAK_MFMA_BF16_TFLOPS if kind == "flop" else PEAK_HBM_GBS, "unit": d["unit"],
+                           "frac": d["frac"], "traffic": traffic, "kernel": dom, "avg_ms": d["avg_ms"],
+                           "work_per_launch": work[dom][1], "work_unit": kind}
+    out["kernels"] = kernels
+    out["drops"] = {"send_dropped": rep["send_dropped"], "recv_dropped": rep["recv_dropped"],
+                    "send_kept": rep["send_kept"], "recv_kept": rep["recv_kept"]}
+    out["source_digest"] = source_digest()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.config, args.seed, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(args.config, args.seed,
+                                           min(args.cpu_tokens, sh.tokens) if args.cpu_tokens else sh.tokens)
     print(json.dumps(out))
 
 

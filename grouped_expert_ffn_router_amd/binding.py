@@ -18,7 +18,8 @@ MOE_ACT_BF16, MOE_ACT_F32 = 0, 1
 MOE_MAX_RANKS, MOE_MAX_LOCAL = 1024, 64
 
 ENTRY_POINTS = ["moe_capacity", "moe_workspace_size", "moe_route", "moe_pack_pools", "moe_recv_waves",
-                "moe_expert_gemm", "moe_combine", "moe_drop_stats", "moe_last_error"]
+                "moe_expert_gemm", "moe_combine", "moe_drop_stats", "moe_last_error", "moe_timing_enable",
+                "moe_timing_read"]
 
 
 class MoeError(RuntimeError):
@@ -52,6 +53,10 @@ class DropReport(ctypes.Structure):
                     expert_arrivals=list(self.expert_arrivals[:X]), expert_kept=list(self.expert_kept[:X]))
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -78,8 +83,11 @@ def lib():
     L.moe_drop_stats.argtypes = [DP, _P, ctypes.POINTER(DropReport), _P]
     L.moe_last_error.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
-    for n in ENTRY_POINTS[:-1]:
-        getattr(L, n).restype = ctypes.c_int
+    L.moe_timing_enable.argtypes = [_I32]
+    L.moe_timing_read.argtypes = [ctypes.POINTER(KernelTime), _I32, ctypes.POINTER(_I32)]
+    for n in ENTRY_POINTS:
+        if n != "moe_last_error":
+            getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
 
@@ -172,3 +180,16 @@ def drop_stats(dims, ws, stream=None, raise_on_bad_ids=True):
 
 def last_error():
     return lib().moe_last_error().decode()
+
+
+def timing_enable(on=True):
+    """Record every library kernel launch with HIP events on its own stream."""
+    _check(lib().moe_timing_enable(1 if on else 0))
+
+
+def timing_read(max_entries=64):
+    """{label: (launches, total_ms)} since the last read (waits for the events)."""
+    buf = (KernelTime * max_entries)()
+    n = _I32()
+    _check(lib().moe_timing_read(buf, max_entries, ctypes.byref(n)))
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n.value, max_entries))}

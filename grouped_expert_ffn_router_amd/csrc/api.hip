@@ -3,8 +3,11 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "moe.h"
 #include "gemm.h"
@@ -34,6 +37,82 @@ int hip_fail(hipError_t e, const char* where) {
 #define HIP_TRY(expr, where)                    \
   do {                                          \
     hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+// ---------------------------------------------------------------- kernel timing
+// While enabled, every launch is bracketed by two HIP events recorded on the
+// launch stream (moe_timing_enable / moe_timing_read).
+
+struct TimingRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TimingRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+class KernelTimer {  // scope guard around one launch
+ public:
+  KernelTimer(const char* name, hipStream_t st) : st_(st) {
+    Timing& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (!t.on) return;
+    rec_.name = name;
+    rec_.start = t.get();
+    rec_.stop = t.get();
+    if (!rec_.start || !rec_.stop || hipEventRecord(rec_.start, st) != hipSuccess) {
+      if (rec_.start) t.pool.push_back(rec_.start);
+      if (rec_.stop) t.pool.push_back(rec_.stop);
+      return;
+    }
+    armed_ = true;
+  }
+  ~KernelTimer() {
+    if (!armed_) return;
+    Timing& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (hipEventRecord(rec_.stop, st_) == hipSuccess) {
+      t.recs.push_back(rec_);
+    } else {
+      t.pool.push_back(rec_.start);
+      t.pool.push_back(rec_.stop);
+    }
+  }
+
+ private:
+  hipStream_t st_;
+  TimingRec rec_{};
+  bool armed_ = false;
+};
+
+// Launch `expr` (a hipError_t expression) timed under `name`.
+#define LAUNCH(name, st, expr, where)          \
+  do {                                         \
+    hipError_t e_;                             \
+    {                                          \
+      KernelTimer kt_(name, st);               \
+      e_ = (expr);                             \
+    }                                          \
     if (e_ != hipSuccess) return hip_fail(e_, where); \
   } while (0)
 
@@ -148,9 +227,10 @@ P* at(void* ws, size_t off) { return (P*)((char*)ws + off); }
 // ---------------------------------------------------------------- GEMM runners
 
 template <bool GATEUP, class A, class B, class E>
-hipError_t gemm_bf16(A a, B b, E e, int N, int K, int64_t max_rows, int groups, hipStream_t st) {
+hipError_t gemm_bf16(const char* name, A a, B b, E e, int N, int K, int64_t max_rows, int groups, hipStream_t st) {
   using Cfg = TileCfg<256, 256>;
   if (N <= 0 || max_rows <= 0 || groups <= 0) return hipSuccess;
+  KernelTimer kt(name, st);
   const int64_t tiles_m = ceil_div(max_rows, Cfg::BM), tiles_n = ceil_div(N, Cfg::BN);
   const int64_t nb = groups * tiles_m * tiles_n;
   hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, GATEUP, A, B, E>), dim3((unsigned)nb), dim3(Cfg::NT), 0, st, a, b, e, N,
@@ -159,9 +239,10 @@ hipError_t gemm_bf16(A a, B b, E e, int N, int K, int64_t max_rows, int groups, 
 }
 
 template <bool GATEUP, class A, class B, class E>
-hipError_t gemm_f32(A a, B b, E e, int N, int K, int64_t max_rows, int groups, hipStream_t st) {
+hipError_t gemm_f32(const char* name, A a, B b, E e, int N, int K, int64_t max_rows, int groups, hipStream_t st) {
   const int cols = GATEUP ? N / 2 : N;
   if (cols <= 0 || max_rows <= 0 || groups <= 0) return hipSuccess;
+  KernelTimer kt(name, st);
   const dim3 grid((unsigned)ceil_div(cols, 16), (unsigned)ceil_div(max_rows, 16), (unsigned)groups);
   hipLaunchKernelGGL((gemm_f32_simple<GATEUP, A, B, E>), grid, dim3(16, 16), 0, st, a, b, e, N, K);
   return hipGetLastError();
@@ -174,8 +255,8 @@ hipError_t route_gemm(const Q& q, const void* x, const void* wr, const void* wd,
   ARows<T> a{(const T*)x, q.D, 0, nullptr, (int)q.T};
   BTwo<T> b{(const T*)wr, (const T*)wd, (int)q.E, q.D};
   ERouteDown<T> e{logits, (T*)z, bias, (int)q.E, (int)q.L, brt};
-  if constexpr (sizeof(T) == 2) return gemm_bf16<false>(a, b, e, (int)(q.E + q.L), (int)q.D, q.T, 1, st);
-  else return gemm_f32<false>(a, b, e, (int)(q.E + q.L), (int)q.D, q.T, 1, st);
+  if constexpr (sizeof(T) == 2) return gemm_bf16<false>("route_gemm", a, b, e, (int)(q.E + q.L), (int)q.D, q.T, 1, st);
+  else return gemm_f32<false>("route_gemm", a, b, e, (int)(q.E + q.L), (int)q.D, q.T, 1, st);
 }
 
 template <class T, class A>
@@ -189,13 +270,13 @@ hipError_t expert_gemms(const Q& q, A a1, int wave, const int32_t* row_src, cons
   EScatter<T> e2{(char*)ret, ret_src_stride, q.row_bytes, (int)q.scap, row_src, q.rcap};
   hipError_t r;
   if constexpr (sizeof(T) == 2) {
-    r = gemm_bf16<true>(a1, b1, e1, (int)(2 * q.H), (int)q.L, q.rcap, (int)q.WX, st);
+    r = gemm_bf16<true>("expert_gate_up", a1, b1, e1, (int)(2 * q.H), (int)q.L, q.rcap, (int)q.WX, st);
     if (r != hipSuccess) return r;
-    return gemm_bf16<false>(a2, b2, e2, (int)q.L, (int)q.H, q.rcap, (int)q.WX, st);
+    return gemm_bf16<false>("expert_down", a2, b2, e2, (int)q.L, (int)q.H, q.rcap, (int)q.WX, st);
   } else {
-    r = gemm_f32<true>(a1, b1, e1, (int)(2 * q.H), (int)q.L, q.rcap, (int)q.WX, st);
+    r = gemm_f32<true>("expert_gate_up", a1, b1, e1, (int)(2 * q.H), (int)q.L, q.rcap, (int)q.WX, st);
     if (r != hipSuccess) return r;
-    return gemm_f32<false>(a2, b2, e2, (int)q.L, (int)q.H, q.rcap, (int)q.WX, st);
+    return gemm_f32<false>("expert_down", a2, b2, e2, (int)q.L, (int)q.H, q.rcap, (int)q.WX, st);
   }
 }
 
@@ -212,16 +293,16 @@ hipError_t shared_and_up(const Q& q, const void* x, const void* ws13, const void
   hipError_t r;
   if constexpr (sizeof(T) == 2) {
     if (q.S > 0) {
-      r = gemm_bf16<true>(a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
+      r = gemm_bf16<true>("shared_gate_up", a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
       if (r != hipSuccess) return r;
     }
-    return gemm_bf16<false>(a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
+    return gemm_bf16<false>("up_shared_down", a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
   } else {
     if (q.S > 0) {
-      r = gemm_f32<true>(a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
+      r = gemm_f32<true>("shared_gate_up", a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
       if (r != hipSuccess) return r;
     }
-    return gemm_f32<false>(a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
+    return gemm_f32<false>("up_shared_down", a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
   }
 }
 
@@ -232,6 +313,53 @@ hipError_t shared_and_up(const Q& q, const void* x, const void* ws13, const void
 extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_timing_enable(int32_t on) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.on = on != 0;
+  return MOE_OK;
+}
+
+int moe_timing_read(moe_kernel_time* out, int32_t max_entries, int32_t* n_entries) {
+  if (!n_entries || (max_entries > 0 && !out) || max_entries < 0)
+    return fail(MOE_EINVAL, "moe_timing_read: bad output arguments");
+  Timing& t = timing();
+  std::vector<TimingRec> recs;
+  {
+    std::lock_guard<std::mutex> g(t.mu);
+    recs.swap(t.recs);
+  }
+  std::vector<moe_kernel_time> acc;
+  hipError_t err = hipSuccess;
+  for (const TimingRec& r : recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    size_t i = 0;
+    while (i < acc.size() && strncmp(acc[i].name, r.name, sizeof(acc[i].name)) != 0) ++i;
+    if (i == acc.size()) {
+      moe_kernel_time k{};
+      snprintf(k.name, sizeof(k.name), "%s", r.name);
+      acc.push_back(k);
+    }
+    acc[i].launches += 1;
+    acc[i].total_ms += ms;
+  }
+  {
+    std::lock_guard<std::mutex> g(t.mu);
+    for (const TimingRec& r : recs) {
+      t.pool.push_back(r.start);
+      t.pool.push_back(r.stop);
+    }
+  }
+  if (err != hipSuccess) return hip_fail(err, "moe_timing_read");
+  const int n = (int)acc.size() < max_entries ? (int)acc.size() : max_entries;
+  for (int i = 0; i < n; ++i) out[i] = acc[i];
+  *n_entries = (int32_t)acc.size();
+  return MOE_OK;
+}
 
 int moe_capacity(const moe_dims* dims, int64_t* send_cap, int64_t* recv_cap, int64_t* pool_stride_bytes) {
   Q q;
@@ -270,7 +398,7 @@ int moe_route(const moe_dims* dims, const void* x, const void* w_router, const v
   HIP_TRY(q.bf16 ? route_gemm<bf16_t>(q, x, w_router, w_down, bias, bias_row_tokens, lg, z, st)
                  : route_gemm<float>(q, x, w_router, w_down, bias, bias_row_tokens, lg, z, st),
           "moe_route gemm");
-  HIP_TRY(launch_select_topk(lg, (int)q.T, (int)q.E, (int)q.k, topk_idx, topk_w, st), "moe_route select");
+  LAUNCH("select_topk", st, launch_select_topk(lg, (int)q.T, (int)q.E, (int)q.k, topk_idx, topk_w, st), "moe_route select");
   return MOE_OK;
 }
 
@@ -286,11 +414,11 @@ int moe_pack_pools(const moe_dims* dims, const void* z, const int32_t* topk_idx,
   const WsLayout w = layout(q);
   hipStream_t st = (hipStream_t)stream;
   int32_t* ctr = at<int32_t>(ws, w.ctr);
-  HIP_TRY(launch_send_rank(topk_idx, (int)(q.T * q.k), (int)q.X, (int)q.E, (int)q.R, at<int32_t>(ws, w.s_lr),
+  LAUNCH("send_rank", st, launch_send_rank(topk_idx, (int)(q.T * q.k), (int)q.X, (int)q.E, (int)q.R, at<int32_t>(ws, w.s_lr),
                            at<int32_t>(ws, w.s_cc), st), "moe_pack_pools rank");
-  HIP_TRY(launch_send_scan(at<int32_t>(ws, w.s_cc), w.nch_s, (int)q.R, (int)q.scap, at<int32_t>(ws, w.s_cb), ctr,
+  LAUNCH("send_scan", st, launch_send_scan(at<int32_t>(ws, w.s_cc), w.nch_s, (int)q.R, (int)q.scap, at<int32_t>(ws, w.s_cb), ctr,
                            send_count, st), "moe_pack_pools scan");
-  HIP_TRY(launch_pack(z, q.row_bytes, topk_idx, at<int32_t>(ws, w.s_lr), at<int32_t>(ws, w.s_cb), (int)q.T,
+  LAUNCH("pack", st, launch_pack(z, q.row_bytes, topk_idx, at<int32_t>(ws, w.s_lr), at<int32_t>(ws, w.s_cb), (int)q.T,
                       (int)q.k, (int)q.X, (int)q.E, (int)q.R, (int)q.scap, send_pools, dst_stride_bytes, q.prow,
                       slot_of, send_count, st), "moe_pack_pools pack");
   return MOE_OK;
@@ -313,16 +441,16 @@ int moe_recv_waves(const moe_dims* dims, const void* recv_pools, int64_t src_str
   const int j0 = wave * (int)q.WX, nj = (int)q.WX, n_rows = (int)(q.R * q.scap);
   int32_t* arrivals = ctr + Ctr::HEADER + 2 * q.R;
   int32_t* kept = arrivals + q.X;
-  HIP_TRY(launch_recv_rank(recv_pools, src_stride_bytes, q.prow, q.row_bytes, (int)q.R, (int)q.scap, (int)q.X,
+  LAUNCH("recv_rank", st, launch_recv_rank(recv_pools, src_stride_bytes, q.prow, q.row_bytes, (int)q.R, (int)q.scap, (int)q.X,
                            (int)q.my_rank, at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cc),
                            st), "moe_recv_waves rank");
-  HIP_TRY(launch_recv_scan(at<int32_t>(ws, w.r_cc), w.nch_r, (int)q.X, (int)q.rcap, j0, nj, at<int32_t>(ws, w.r_cb),
+  LAUNCH("recv_scan", st, launch_recv_scan(at<int32_t>(ws, w.r_cc), w.nch_r, (int)q.X, (int)q.rcap, j0, nj, at<int32_t>(ws, w.r_cb),
                            arrivals, kept, ctr + Ctr::RECV_BAD, wave_count, st), "moe_recv_waves scan");
-  HIP_TRY(launch_recv_place(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cb), n_rows,
+  LAUNCH("recv_place", st, launch_recv_place(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cb), n_rows,
                             (int)q.X, (int)q.rcap, j0, nj, wave_count, at<int32_t>(ws, w.r_rank), row_src, st),
           "moe_recv_waves place");
   if (wave_buf)
-    HIP_TRY(launch_wave_gather(recv_pools, src_stride_bytes, q.prow, (int)q.scap, q.row_bytes, row_src, wave_count,
+    LAUNCH("wave_gather", st, launch_wave_gather(recv_pools, src_stride_bytes, q.prow, (int)q.scap, q.row_bytes, row_src, wave_count,
                                nj, (int)q.rcap, wave_buf, st), "moe_recv_waves gather");
   return MOE_OK;
 }
@@ -368,7 +496,7 @@ int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf, co
     }
   }
   HIP_TRY(r, "moe_expert_gemm gemm");
-  HIP_TRY(launch_zero_dropped(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_rank), (int)(q.R * q.scap), (int)q.scap,
+  LAUNCH("zero_dropped", st, launch_zero_dropped(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_rank), (int)(q.R * q.scap), (int)q.scap,
                               (int)q.rcap, wave * (int)q.WX, (int)q.WX, ret_pools, ret_src_stride_bytes, q.row_bytes,
                               st), "moe_expert_gemm zero rows");
   return MOE_OK;
@@ -390,7 +518,7 @@ int moe_combine(const moe_dims* dims, const void* ret_pools, int64_t ret_dst_str
   hipStream_t st = (hipStream_t)stream;
   void* cat = at<char>(ws, w.cat);
   const int64_t ldc = q.L + q.S * q.HS;
-  HIP_TRY(launch_combine(q.bf16 ? 0 : 1, ret_pools, ret_dst_stride_bytes, q.row_bytes, (int)q.scap, slot_of, topk_w,
+  LAUNCH("combine", st, launch_combine(q.bf16 ? 0 : 1, ret_pools, ret_dst_stride_bytes, q.row_bytes, (int)q.scap, slot_of, topk_w,
                          (int)q.T, (int)q.k, (int)q.L, cat, ldc, st), "moe_combine combine");
   HIP_TRY(q.bf16 ? shared_and_up<bf16_t>(q, x, ws13, ws2, w_up, (bf16_t*)cat, out, st)
                  : shared_and_up<float>(q, x, ws13, ws2, w_up, (float*)cat, out, st),

@@ -187,6 +187,29 @@ int moe_drop_stats(const moe_dims* dims, const void* ws, moe_drop_report* report
 /* Thread-local message of the last failed call ("" if none). */
 const char* moe_last_error(void);
 
+/* Per-kernel timing, a measurement aid for the layer above (not part of the
+ * layer's arithmetic).  While enabled, every kernel launched by the calls
+ * above is bracketed by two HIP events recorded on the stream it is launched
+ * on, so the elapsed time between them is that kernel's duration on its own
+ * stream.  Enabling adds two event records per launch; results are unchanged.
+ * Labels: route_gemm, select_topk, send_rank, send_scan, pack, recv_rank,
+ * recv_scan, recv_place, wave_gather, expert_gate_up, expert_down,
+ * zero_dropped, combine, shared_gate_up, up_shared_down. */
+typedef struct moe_kernel_time {
+  char name[32];    /* kernel label */
+  int32_t launches; /* launches recorded since the last moe_timing_read */
+  double total_ms;  /* their summed durations */
+} moe_kernel_time;
+
+/* Turn recording on (on != 0) or off for the whole process.  Never fails. */
+int moe_timing_enable(int32_t on);
+
+/* Wait for every recorded launch, write up to max_entries per-label totals to
+ * out (labels in first-launch order), set *n_entries to the number of labels
+ * recorded, and clear the record.  MOE_EINVAL for NULL or negative
+ * arguments; MOE_EHIP if an event cannot be read. */
+int moe_timing_read(moe_kernel_time* out, int32_t max_entries, int32_t* n_entries);
+
 #ifdef __cplusplus
 }
 #endif
