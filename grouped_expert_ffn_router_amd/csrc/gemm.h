@@ -6,12 +6,11 @@
 //
 // bf16 path (gfx950): one 256-thread workgroup (4 waves, 2 x 2) per BM x BN
 // output tile; each wave owns a (BM/2) x (BN/2) sub-tile built from
-// v_mfma_f32_32x32x16_bf16.  K advances in steps of 64: the next step's
-// operands go straight from HBM into the second LDS buffer (direct 16-byte
-// global->LDS loads, each group of 8 lanes reading one full 128-byte row
-// segment) while the current step's MFMAs run.  LDS rows are 128 bytes
-// with the 16-byte chunk index XOR-swizzled per row, so the fragment reads
-// of any 8 (or 16) consecutive lanes touch every LDS bank once.
+// v_mfma_f32_32x32x16_bf16.  K advances in steps of 64 through two LDS
+// buffers filled straight from HBM (16-byte global->LDS loads, each group of
+// 8 lanes reading one 128-byte row segment) one step ahead of the MFMAs.
+// LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled per row,
+// so the fragment reads run at the bank-conflict-free rate.
 // The MFMA is issued with the B fragment as its first operand, so every lane
 // ends up holding one output row m and runs of 4 consecutive columns n: the
 // epilogue stores 8-byte pieces and resolves a row's destination once.
@@ -232,13 +231,15 @@ struct EStore {
 
 template <int BM_, int BN_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int BM = BM_, BN = BN_, BK = 64;       // 2 LDS buffers of BK-deep tiles
   static constexpr int NT = 256;                          // 4 waves, 2 x 2
   static constexpr int WTM = BM / 2, WTN = BN / 2;        // wave sub-tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;      // 32x32 fragments per wave
   static constexpr int LA = BM / 32, LB = BN / 32;        // 16-byte loads per lane per K step
-  static constexpr int STAGE = (BM + BN) * 128;           // bytes of one LDS buffer
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sides are multiples of 64");
+  static constexpr int ROW = BK * 2;                      // bytes of one LDS row (128)
+  static constexpr int STAGE = (BM + BN) * ROW;           // bytes of one LDS buffer
+  static_assert(BM == 256 && BN == 256, "the loader and fragment layout assume 256 x 256 tiles");
+  static_assert(2 * STAGE <= 160 * 1024, "LDS budget of one workgroup");
 };
 
 // Logical tile of workgroup `bid`: XCD-contiguous ranges, M-grouped order
@@ -277,29 +278,51 @@ __device__ __forceinline__ void lgkm_wait(bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
                : "memory");
 }
 
-// 16-byte chunk swizzle of a 128-byte LDS row.  Rows r and r' with the same
-// swizzle never share a 16-lane (64-bank) or an 8-lane (32-bank) read group:
-// f(r) = (r >> 1) ^ 4 (r & 1) is a permutation of 0..7 over any 8 consecutive
-// rows and over any 8 rows of one parity among 16 consecutive rows.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
+// Workgroup barrier without a memory fence.  __syncthreads() would also wait
+// for every outstanding load, including the HBM->LDS loads of later steps
+// that must stay in flight; the LDS data a barrier publishes here was
+// awaited explicitly (vm_wait) by the lane that loaded it, and LDS is
+// coherent within the workgroup.
+__device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
+
+// Wait until at most N vector-memory loads (here: HBM->LDS loads) of this
+// lane are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// 16-byte chunk swizzle of a 128-byte LDS row (8 chunks): chunk c of row r
+// is stored at c ^ ((r >> 1) & 7).  Measured on gfx950 with the fragment read
+// pattern below (32 rows x 2 chunks per instruction), this keeps 16-byte LDS
+// reads at the bank-conflict-free rate (about 250 B/clk per CU); unswizzled
+// rows run 8-way conflicted and r & 7 2-way.  Rows 16 apart share it.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // grid: (groups * tiles_m * tiles_n); block: 256.  K must be a multiple of 64.
 // GATEUP: N counts gate+up columns (blocks of 64) and the epilogue gets
 // (gate, up) pairs.
 //
-// One K step (64) of the main loop: wait for this step's tiles to land in LDS
-// and pass the barrier; issue every fragment read of the step; then issue the
-// direct HBM->LDS loads of the next step into the other buffer (nobody reads
-// that buffer any more: all its fragment reads were consumed before the
-// barrier); then run the step's MFMAs while those loads are in flight.
-// Issuing the loads after the reads keeps them off the reads' dependence
-// path, and no staging registers are needed.
+// Pipeline: two LDS buffers of 64-deep K steps.  A step is 4 substeps of
+// k16, each 16 MFMAs per wave on one set of fragments.  With one wave per
+// SIMD the instruction stream issues in order, so every LDS read and every
+// HBM->LDS load sits between two MFMAs (pinned by scheduling fences): a
+// stalled issue never leaves the MFMA pipe without queued work.  Substep s
+// reads the fragments of substep s+1; substeps 0 and 1 also issue the loads of
+// the next step into the other buffer (free: every wave finished reading it
+// before the barrier that opened this step); the last substep waits for those
+// loads, passes the barrier and reads the first fragments of the next step.
+// Loads move 128-byte row segments (whole L2 lines); each wave's blocks are
+// contiguous in LDS so one M0 value serves four loads through the
+// instruction's immediate offset (which also shifts the HBM address; it is
+// subtracted from the row pointers up front).
 template <class Cfg, bool GATEUP, class A, class B, class E>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WTM = Cfg::WTM, WTN = Cfg::WTN;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, LA = Cfg::LA, LB = Cfg::LB, STAGE = Cfg::STAGE;
-  constexpr int KS = BK / 16;
+  constexpr int ROW = Cfg::ROW, NLOAD = LA + LB;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   int g, tm, tn;
@@ -310,44 +333,29 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Loader: load slot i of a wave fills the 1 KB LDS block i*4 + wave, i.e.
-  // rows r = (i*4 + wave)*8 + lane/8, lane landing at block + 16*lane.  That
-  // LDS position holds swizzled chunk lane%8 of row r, so the lane fetches
-  // global chunk (lane%8) ^ swz(r); all rows of a lane are 32 apart and share
-  // the swizzle.
+  // wave w owns the 8 LDS blocks (1 KB = 8 rows) w*8 .. w*8+7 of A and of B:
+  // slot d holds rows w*64 + d*8 + lane/8, lane lands at block + 16*lane.
   const int lrow = lane >> 3, lcol = lane & 7;
-  const int r0 = wave * 8 + lrow;
-  const int gcol = (lcol ^ swz(r0)) * 8;
   const bf16_t* pa[LA];
+  int gcola[2];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) pa[i] = a.row(g, min(m0 + r0 + 32 * i, M - 1)) + gcol;
+  for (int p = 0; p < 2; ++p) gcola[p] = (lcol ^ swz(wave * 64 + p * 8 + lrow)) * 8;
+#pragma unroll
+  for (int d = 0; d < LA; ++d)
+    pa[d] = a.row(g, min(m0 + wave * 64 + d * 8 + lrow, M - 1)) + gcola[d & 1] - 512 * (d & 3);
   const bf16_t* pb[LB];
   int nb_row[LB];
 #pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    nb_row[i] = min(n0 + r0 + 32 * i, N - 1);
-    pb[i] = b.ptr(g, nb_row[i], gcol);
+  for (int d = 0; d < LB; ++d) {
+    nb_row[d] = min(n0 + wave * 64 + d * 8 + lrow, N - 1);
+    pb[d] = b.ptr(g, nb_row[d], gcola[d & 1]) - 512 * (d & 3);
   }
-  auto dma = [&](int st, int k0) {
-    char* s = smem + st * STAGE + wave * 1024;
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(pa[i] + k0), (__attribute__((address_space(3))) void*)(s + i * 4096),
-                                       16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const bf16_t* p = B::KSEG ? b.ptr(g, nb_row[i], k0 + gcol) : pb[i] + k0;
-      __builtin_amdgcn_global_load_lds((const void*)p,
-                                       (__attribute__((address_space(3))) void*)(s + BM * 128 + i * 4096), 16, 0, 0);
-    }
-  };
+  const int nk = K / BK;
 
-  // Fragment reads: lane reads row (base + lane%32), 16-byte chunk ks*2 + lane/32.
-  // Fragment rows are 32 apart, so one swizzle serves them all.
   const int frow = lane & 31, fhalf = lane >> 5;
   const int fswz = swz(frow);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
-  const uint32_t fa_base = lds0 + (wm * WTM + frow) * 128, fb_base = lds0 + BM * 128 + (wn * WTN + frow) * 128;
+  const uint32_t fa_base = lds0 + (wm * WTM + frow) * ROW, fb_base = lds0 + BM * ROW + (wn * WTN + frow) * ROW;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -357,52 +365,76 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // The fragment reads are issued as inline ds_read_b128 so that the
-  // compiler, which cannot tell the two LDS buffers apart, does not make
-  // them wait for the in-flight HBM->LDS loads of the other buffer; their
-  // completion is awaited explicitly (lgkm_wait ties the fragments, so no
-  // MFMA can be scheduled before the wait that covers its operands).
-  bf16x8 fa[KS][FM], fb[KS][FN];
-  auto read_step = [&](uint32_t st_off, int ks) {
-    const uint32_t ch = (uint32_t)(((ks * 2 + fhalf) ^ fswz) << 4) + st_off;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) lds_read16(fa[ks][i], fa_base + ch + i * 4096);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) lds_read16(fb[ks][j], fb_base + ch + j * 4096);
+  struct Frags {
+    bf16x8 a[FM], b[FN];
   };
-  auto mma_step = [&](int ks) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+  constexpr int NF = FM + FN, NMMA = FM * FN, KS = BK / 16;
+  auto read1 = [&](Frags& f, int kt, int ks, int q) {
+    const uint32_t st = (uint32_t)((kt & 1) * STAGE) + (uint32_t)(((ks * 2 + fhalf) ^ fswz) << 4);
+    if (q < FM) lds_read16(f.a[q], fa_base + st + q * 32 * ROW);
+    else lds_read16(f.b[q - FM], fb_base + st + (q - FM) * 32 * ROW);
   };
-
-  const int nk = K / BK;
-  dma(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // next step's tiles go to the other buffer, whose last reads completed
-    // before the barrier; the last step re-fetches its own slice there
-    dma((kt + 1) & 1, min(kt + 1, nk - 1) * BK);
-    const uint32_t st_off = (kt & 1) * STAGE;
-    read_step(st_off, 0);
-    read_step(st_off, 1);
-    lgkm_wait<FM + FN>(fa[0], fb[0]);
-    mma_step(0);
-#pragma unroll
-    for (int ks = 1; ks < KS; ++ks) {
-      if (ks + 1 < KS) {
-        read_step(st_off, ks + 1);
-        lgkm_wait<FM + FN>(fa[ks], fb[ks]);
-      } else {
-        lgkm_wait<0>(fa[ks], fb[ks]);
-      }
-      mma_step(ks);
+  auto load1 = [&](int kt, int d) {  // d in [0, NLOAD)
+    const int k0 = min(kt, nk - 1) * BK;
+    char* s = smem + (kt & 1) * STAGE;
+    const void* gp;
+    char* lp;
+    const int dd = d < LA ? d : d - LA;
+    if (d < LA) {
+      gp = (const void*)(pa[dd] + k0);
+      lp = s + wave * 8192 + (dd >> 2) * 4096;
+    } else {
+      gp = (const void*)(B::KSEG ? b.ptr(g, nb_row[dd], k0 + gcola[dd & 1]) - 512 * (dd & 3) : pb[dd] + k0);
+      lp = s + BM * ROW + wave * 8192 + (dd >> 2) * 4096;
     }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write outlives the loop
+    auto l3 = (__attribute__((address_space(3))) void*)lp;
+    switch (dd & 3) {
+      case 0: __builtin_amdgcn_global_load_lds(gp, l3, 16, 0, 0); break;
+      case 1: __builtin_amdgcn_global_load_lds(gp, l3, 16, 1024, 0); break;
+      case 2: __builtin_amdgcn_global_load_lds(gp, l3, 16, 2048, 0); break;
+      default: __builtin_amdgcn_global_load_lds(gp, l3, 16, 3072, 0); break;
+    }
+  };
+  auto mma1 = [&](const Frags& f, int q) {
+    const int i = q / FN, j = q % FN;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+  Frags F[KS];
+  // step kt: enters with the reads of substep 0 (F[0]) issued and step kt's
+  // tiles visible; the loads of step kt+1 go out during substeps 0..1.
+  auto step = [&](int kt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
+        lgkm_wait<0>(F[ks].a, F[ks].b);
+#pragma unroll
+        for (int q = 0; q < NMMA; ++q) {
+          mma1(F[ks], q);
+          if (q < NF) read1(F[ks + 1], kt, ks + 1, q);
+          else if (ks * (NMMA - NF) + (q - NF) < NLOAD) load1(kt + 1, ks * (NMMA - NF) + (q - NF));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        lgkm_wait<0>(F[ks].a, F[ks].b);
+        vm_wait<0>();                         // step kt+1's tiles (this lane's part)
+        lds_barrier();                        // ... every lane's; step kt's buffer is free
+#pragma unroll
+        for (int q = 0; q < NMMA; ++q) {
+          mma1(F[ks], q);
+          if (q < NF) read1(F[0], kt + 1, 0, q);  // past the last step: a stale buffer, unused
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < NLOAD; ++d) load1(0, d);
+  vm_wait<0>();
+  lds_barrier();
+#pragma unroll
+  for (int q = 0; q < NF; ++q) read1(F[0], 0, 0, q);
+  for (int kt = 0; kt < nk; ++kt) step(kt);
+  vm_wait<0>();
 
   // Accumulator layout (B fragment first): lane holds row m = base + lane%32 and
   // columns n = base + 8*(v/4) + 4*(lane/32) + v%4.
