@@ -216,7 +216,7 @@ def _oracle_token_out(sh, inp, ref, tokens):
     return z, exact
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_one_rank_full_size(runner, cfg):
     sh = configs.get(cfg)
     scap, rcap = O.capacities(sh)
@@ -244,6 +244,8 @@ def test_one_rank_full_size(runner, cfg):
     assert rep["recv_dropped"] == rv["recv_dropped"].sum() and rep["recv_bad_ids"] == 0
     if cfg == 4:
         assert rep["send_dropped"] > 0 and rep["recv_dropped"] > 0
+    if cfg == 5:
+        assert rep["send_dropped"] > 0  # segment-correlated routing overflows some pools
     # sampled float checks
     rng = np.random.default_rng(cfg)
     tokens = np.unique(np.concatenate([[0, sh.tokens - 1], rng.choice(sh.tokens, 30, replace=False)]))
