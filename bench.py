@@ -119,6 +119,8 @@ def cpu_baseline(cfg, seed, tokens):
     sh = configs.with_tokens(base, tokens) if tokens != base.tokens else base
     scap, _ = O.capacities(sh)
     inp = gen.generate(sh, seed=seed, send_cap=scap)
+    if "sources" in inp:  # the other ranks' pools: their dispatch is not this rank's work (untimed)
+        inp["foreign_ids"], inp["foreign_rows"], _ = O.routed_source_pools(sh, inp, with_rows=sh.layer == "full")
     threads = os.cpu_count()
     try:
         from threadpoolctl import threadpool_info

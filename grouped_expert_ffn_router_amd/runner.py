@@ -6,9 +6,12 @@ are provided:
 
 * ``OneRankLayer``: one rank's share at its real shape.  The rank's own
   tokens go through route -> pack; its receive buffer holds its own pool for
-  itself plus the pools the other ranks sent (inputs); its combine reads the
-  rows it computed for itself plus the rows the other ranks returned
-  (inputs).  The only copies are the self-blocks of the two exchanges.
+  itself plus the pools the other ranks sent; its combine reads the rows it
+  computed for itself plus the rows the other ranks returned (inputs).  When
+  the workload gives the other ranks' tokens, their pools are made at set-up
+  by running those ranks' route -> pack through the same library calls
+  (untimed: it stands for what the other GPUs do); otherwise they are
+  inputs.  The only copies in a step are the self-blocks of the exchanges.
 * ``AllRanksLayer``: every rank of a small domain on one device.  All send
   pools sit in one [R_src][R_dst][send_cap][stride] block and all return rows
   in one [R_recv][R_src][send_cap][L] block, so each exchange is a strided
@@ -79,8 +82,12 @@ class OneRankLayer:
         self.send_pools = torch.empty((R, self.scap, self.prow), dtype=torch.uint8, device=dev)
         self.slot_of = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.send_count = torch.empty((R,), dtype=torch.int32, device=dev)
-        # receive side: pools from the other ranks are inputs; slot r is our own pool
-        self.recv_pools = upload(pool_block_host(inp["foreign_ids"], inp["foreign_rows"], self.prow, shape.act), dev)
+        # receive side: slot s holds the pool source s sent; slot r is our own pool
+        if "sources" in inp:
+            self.recv_pools = torch.zeros((R, self.scap, self.prow), dtype=torch.uint8, device=dev)
+        else:
+            self.recv_pools = upload(pool_block_host(inp["foreign_ids"], inp["foreign_rows"], self.prow, shape.act),
+                                     dev)
         self.row_src = torch.empty((W, WX, self.rcap), dtype=torch.int32, device=dev)
         self.wave_count = torch.empty((W, WX), dtype=torch.int32, device=dev)
         self.wave_buf = torch.empty((WX, self.rcap, L), dtype=act, device=dev) if gather == "buffer" else None
@@ -94,6 +101,29 @@ class OneRankLayer:
             self.ret_send = torch.zeros((R, self.scap, L), dtype=act, device=dev)
             self.ret_recv = upload(inp["foreign_ret"], dev)
             self.out = torch.empty((T, D), dtype=act, device=dev)
+        if "sources" in inp:
+            self._route_other_ranks(inp["sources"])
+
+    def _route_other_ranks(self, sources):
+        """Each other rank s routes its own tokens and packs its pools; keep the
+        pool it sends to this rank (uses this layer's dispatch buffers, which
+        the rank's own dispatch overwrites later)."""
+        from concurrent.futures import ThreadPoolExecutor
+        others = [s for s in range(self.shape.n_ranks) if s != self.rank]
+        with ThreadPoolExecutor(max_workers=8) as ex:  # host draws overlap the GPU work
+            drawn = ex.map(sources, others)
+            for s, host_x in zip(others, drawn):
+                self._route_one(s, host_x)
+        torch.cuda.synchronize()
+
+    def _route_one(self, s, host_x):
+        xs = upload(host_x, self.device)
+        d = self.dims
+        B.route(d, xs, self.w_router, self.w_down, self.bias, self.bias_row_tokens, self.logits, self.z,
+                self.idx, self.w, self.ws)
+        B.pack_pools(d, self.z, self.idx, self.send_pools, self.scap * self.prow, self.slot_of, self.send_count,
+                     self.ws)
+        self.recv_pools[s].copy_(self.send_pools[self.rank])
 
     @property
     def esize(self):

@@ -424,13 +424,53 @@ def drop_ledger(shape, disp, recvs):
                 total=R * T * k)
 
 
+def routed_source_pools(shape, inp, with_rows=True):
+    """Pools that every other rank sends to the measured rank, by routing that
+    rank's own tokens through the same router.
+
+    [P1 §二]: each rank routes its tokens and keeps one fixed pool per
+    destination; the measured rank receives pool `receiver` of every source.
+    inp["sources"](s) gives source s's tokens; the measured rank's own pool is
+    left empty here (it comes from the rank's own dispatch).
+    Returns ids [R][send_cap] int32, rows [R][send_cap][L] (float64, zeros
+    where empty; None unless with_rows) and tok [R][send_cap] int32: the
+    source token whose latent fills each slot (-1 for empty slots).
+    """
+    d = _dims(shape)
+    R, X, L = d["R"], d["X"], d["L"]
+    scap, _ = capacities(shape)
+    r = inp["receiver"]
+    ids = np.full((R, scap), -1, dtype=np.int32)
+    tok = np.full((R, scap), -1, dtype=np.int32)
+    rows = np.zeros((R, scap, L)) if with_rows else None
+    for s in range(R):
+        if s == r:
+            continue
+        xs = inp["sources"](s)
+        logits = router_logits(xs, inp["w_router"], inp["bias"], inp["bias_row_tokens"])
+        idx, _ = select_topk(logits, d["k"])
+        sl = send_slots(idx, X, R, scap)
+        pid, _ = pack_pools(idx, sl["slot_of"], R, scap)
+        ids[s] = pid[r]
+        flat = sl["slot_of"].reshape(-1)
+        mine = (flat >= r * scap) & (flat < (r + 1) * scap)
+        slots = flat[mine] - r * scap
+        tokens = np.repeat(np.arange(xs.shape[0]), d["k"])[mine]
+        tok[s, slots] = tokens
+        if with_rows and slots.size:
+            rows[s, slots] = down_project(xs[tokens], inp["w_down"], d["act"])
+    return ids, rows, tok
+
+
 def layer_one_rank(shape, inp, with_floats=True):
     """One rank's share: its own tokens, plus pools/returns of the other ranks as inputs.
 
     The receiver r = inp["receiver"] receives its own pool r (from its own
-    dispatch) and the generated pools of every other source; its combine reads
-    the rows it computed for itself and the generated rows of every other
-    destination.
+    dispatch) and the pools of every other source (inp["foreign_ids"] and,
+    for the float path, inp["foreign_rows"]: drawn by the workload, or
+    computed with routed_source_pools); its combine reads the rows it
+    computed for itself and the rows every other destination returned
+    (inp["foreign_ret"]).
     """
     d = _dims(shape)
     R, X, H, HS, act = d["R"], d["X"], d["H"], d["HS"], d["act"]

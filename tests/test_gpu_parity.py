@@ -222,12 +222,28 @@ def test_one_rank_full_size(runner, cfg):
     scap, rcap = O.capacities(sh)
     _say(f"[full-size] config {cfg} grid=True gather=fused")
     inp = gen.generate(sh, seed=0, grid=True, send_cap=scap)
+    if "sources" in inp:  # draw every rank's tokens once, for the GPU set-up and the oracle
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            drawn = dict(zip(range(sh.n_ranks), ex.map(inp["sources"], range(sh.n_ranks))))
+        inp["sources"] = drawn.__getitem__
     lay = runner.OneRankLayer(sh, inp, gather="fused")
     lay.run()
     torch.cuda.synchronize()
     rep = lay.drop_report()
-    ref = O.layer_one_rank(sh, inp, with_floats=False)
-    d, rv, r = ref["dispatch"], ref["recv"], inp["receiver"]
+    r = inp["receiver"]
+    oin = dict(inp)
+    if "sources" in inp:
+        # the other ranks route their own tokens: the oracle does the same
+        oin["foreign_ids"], oin["foreign_rows"], _ = O.routed_source_pools(sh, inp, with_rows=True)
+        gids, grows = _decode_pools(lay.recv_pools, sh.latent, sh.act)
+        others = [s for s in range(sh.n_ranks) if s != r]
+        assert np.array_equal(gids[others], oin["foreign_ids"][others]), "pools received from routed sources"
+        filled = oin["foreign_ids"][others] >= 0
+        assert np.array_equal(grows[others][filled], oin["foreign_rows"][others][filled]), "received payload rows"
+        del gids, grows
+    ref = O.layer_one_rank(sh, oin, with_floats=False)
+    d, rv = ref["dispatch"], ref["recv"]
     act, L, X, W = sh.act, sh.latent, sh.local_experts, sh.waves
     _check_routing(sh, d, host(lay.logits), host(lay.idx), host(lay.w), True, f"cfg{cfg}")
     assert np.array_equal(host(lay.slot_of), d["slot_of"])
@@ -262,7 +278,7 @@ def test_one_rank_full_size(runner, cfg):
         return
     # returned rows of sampled received rows (from other sources)
     ret = host(lay.ret_send)
-    frows = inp["foreign_rows"]
+    frows = oin["foreign_rows"]
     for w, experts in enumerate(waves):
         for jw, j in enumerate(experts):
             n = rv["count"][j]
@@ -270,8 +286,8 @@ def test_one_rank_full_size(runner, cfg):
                 src, slot = divmod(int(rv["row_src"][j, q]), scap)
                 if src == r:
                     continue
-                y = O.expert_ffn(gen.to_f32(frows[src, slot:slot + 1]).astype(np.float64), inp["w13"][j],
-                                 inp["w2"][j], sh.expert_hidden, act)[0]
+                y = O.expert_ffn(O.f64(frows[src, slot:slot + 1]), inp["w13"][j], inp["w2"][j],
+                                 sh.expert_hidden, act)[0]
                 assert_stored_close(ret[src, slot], y, act, f"returned row ({src},{slot}) expert {j}")
     # layer output for sampled own tokens
     _, out_exact = _oracle_token_out(sh, inp, ref, tokens)

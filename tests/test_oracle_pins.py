@@ -390,6 +390,41 @@ def test_one_rank_layer_matches_all_rank_emulation():
     assert scap == res["send_cap"]
 
 
+def test_routed_source_pools_match_all_rank_emulation():
+    """The pools other ranks send to the measured rank, made by routing their
+    own tokens (one-rank workloads), are exactly the pools those ranks send in
+    the all-rank emulation of the same seed; the per-rank token draws agree."""
+    from dataclasses import replace
+    sh = configs.get("mini_bf16_skew")
+    full_inp = gen.generate(sh, seed=7, grid=True)
+    full = O.layer_all_ranks(sh, full_inp)
+    one_sh = replace(sh, emulate_all_ranks=False, foreign="routed")
+    scap, _ = O.capacities(one_sh)
+    inp = gen.generate(one_sh, seed=7, grid=True, send_cap=scap)
+    r = inp["receiver"]
+    assert r == 0 and np.array_equal(inp["x"], full_inp["x"][r])
+    for s in range(sh.n_ranks):
+        assert np.array_equal(inp["sources"](s), full_inp["x"][s])
+    ids, rows, tok = O.routed_source_pools(one_sh, inp, with_rows=True)
+    for s in range(sh.n_ranks):
+        if s == r:
+            assert np.all(ids[s] == -1) and np.all(tok[s] == -1)
+            continue
+        d = full["dispatch"][s]
+        assert np.array_equal(ids[s], d["pool_ids"][r])
+        assert np.array_equal(rows[s], d["pool_rows"][r])
+        kept = ids[s] >= 0
+        assert np.all((tok[s] >= 0) == kept)
+        # the token of every filled slot really chose that expert
+        assert all(ids[s][q] in d["idx"][tok[s][q]] for q in np.flatnonzero(kept))
+        assert all(r * sh.local_experts <= ids[s][q] < (r + 1) * sh.local_experts for q in np.flatnonzero(kept))
+    # and the one-rank receive of those pools equals rank r's receive in the emulation
+    inp["foreign_ids"] = ids
+    res = O.layer_one_rank(one_sh, inp, with_floats=False)
+    assert np.array_equal(res["recv"]["row_src"], full["recv"][r]["row_src"])
+    assert np.array_equal(res["recv"]["recv_dropped"], full["recv"][r]["recv_dropped"])
+
+
 # ------------------------------------------------------- planted mistakes
 
 

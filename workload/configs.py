@@ -45,6 +45,10 @@ class Shape:
     zipf_std: float = 2.0
     receiver: str = "rank0"           # "rank0" | "hot_expert" (host of argmax bias)
     layer: str = "full"               # "dispatch" (route+pack) | "full"
+    # one-rank workloads: how the other ranks' pools to the measured rank arise
+    #   "routed": every other rank's own seeded tokens go through the same router
+    #   "drawn":  pool contents drawn from a model of the arrivals (see gen.py)
+    foreign: str = "routed"
 
     @property
     def local_experts(self):
@@ -59,7 +63,8 @@ class Shape:
 # one-rank layer at 4K context (8192 tokens = 2 sequences of 4096).  4: the
 # dispatch shape with a Zipf(1.1) per-expert router bias scaled to std 2.
 # 5: one 65536-token sequence per rank with routing correlated inside
-# 512-token segments.
+# 512-token segments.  In 2-4 the other 63 ranks' tokens go through the same
+# router; in 5 (64 x 65536 tokens would be 52 GB) their pools are drawn.
 CONFIGS = {
     1: Shape("cfg1_tiny_f32", tokens=256, d_model=64, latent=32, n_experts=24,
              top_k=2, n_ranks=4, waves=3, expert_hidden=64, shared_experts=1,
@@ -76,7 +81,8 @@ CONFIGS = {
              receiver="hot_expert", layer="dispatch"),
     5: Shape("cfg5_long_context_64k", tokens=65536, d_model=6144, latent=3072,
              n_experts=384, top_k=8, n_ranks=64, waves=3, expert_hidden=1536,
-             shared_experts=2, shared_hidden=1536, act="bf16", bias="segments"),
+             shared_experts=2, shared_hidden=1536, act="bf16", bias="segments",
+             foreign="drawn"),
 }
 
 # Small bf16 workloads for element-by-element parity: several GEMM tiles in

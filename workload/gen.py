@@ -23,12 +23,15 @@ Value recipe (the pages print no data; the shapes are those of the Marin
   ``segment_boost`` to the logits of ``segment_hot`` experts drawn per segment
   without replacement.
 
-For one-rank workloads (configs 2-5) the other 63 ranks are not simulated:
-their send pools towards the measured rank and the results they return are
-drawn directly (see ``foreign_pools`` and ``foreign_returns``), with the row
-counts and expert mix of a near-uniform router (configs 2-3), of a router whose
-hottest expert lives on the measured rank (config 4), or of segment-correlated
-routing (config 5).
+For one-rank workloads (configs 2-5) the measured rank needs the pools the
+other ranks send it.  With ``shape.foreign == "routed"`` (configs 2-4) every
+rank s has its own seeded tokens (``source_tokens``), the very draw that an
+emulation of all ranks would use, and the consumers route them through the
+same router themselves; this module only draws them.  With
+``shape.foreign == "drawn"`` (config 5) the pools are drawn directly from a
+model of the arrivals of segment-correlated routing (``foreign_pools``).  The
+rows the other ranks return for the measured rank's own tokens are drawn in
+both cases (``foreign_returns``).
 """
 
 import numpy as np
@@ -105,8 +108,12 @@ def _normal_parts(seeds, name, n_parts, part_shape, std, act, threads=8):
 
 
 def _grid_x(rng, shape):
-    a = np.clip(np.rint(rng.standard_normal(size=shape) * 4.0), -8, 8)
-    return (a / 4.0).astype(np.float32)
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    a *= np.float32(4.0)
+    np.rint(a, out=a)
+    np.clip(a, -8, 8, out=a)
+    a *= np.float32(0.25)
+    return a
 
 
 def _grid_w(rng, shape, fan_in):
@@ -142,6 +149,16 @@ def _segment_bias(rng, T, E, seg_tokens, hot, boost):
 # ---------------------------------------------------------------- inputs
 
 
+def source_tokens(shape: Shape, seed, s, grid=False):
+    """Tokens [T][D] (storage type) of rank s: the same draw for every caller."""
+    sd = _Seeds(seed)
+    T, D = shape.tokens, shape.d_model
+    if grid:
+        return _store(_grid_x(sd.rng("x", s), (T, D)), shape.act)
+    return _store(_normal(sd.rng("x", s), (T, D), 1.0), shape.act)
+
+
+
 def generate(shape: Shape, seed=0, grid=False, send_cap=None, with_foreign=True):
     """All inputs of one workload as numpy arrays (float32 or uint16 bf16 bits).
 
@@ -157,7 +174,10 @@ def generate(shape: Shape, seed=0, grid=False, send_cap=None, with_foreign=True)
       bias       None, [1][E] (zipf) or [nseg][E] (segments), float32
       bias_row_tokens  tokens per bias row (0 = one row for all tokens)
       receiver   measured rank (one-rank workloads)
-      foreign_ids, foreign_rows     pools the other ranks send to the receiver
+      sources    (foreign == "routed") function s -> tokens [T][D] of rank s;
+                 x is sources(receiver)
+      foreign_ids, foreign_rows     (foreign == "drawn") pools the other ranks
+                                    send to the receiver
       foreign_ret                   rows the other ranks return to the receiver
     For one-rank workloads ``send_cap`` (rows per pool) must be given when
     ``with_foreign`` is true; it is an input here, not derived.
@@ -168,17 +188,6 @@ def generate(shape: Shape, seed=0, grid=False, send_cap=None, with_foreign=True)
     act = shape.act
     full = shape.layer == "full"
     out = {}
-
-    # tokens
-    n_src = R if shape.emulate_all_ranks else 1
-    if grid:
-        if not grid_sum_bound_ok(shape):
-            raise ValueError("exact-grid construction needs d_model * 8 * 255 < 2**24")
-        xs = np.stack([_grid_x(sd.rng("x", s), (T, D)) for s in range(n_src)])
-        xs = _store(xs, act)
-    else:
-        xs = _normal_parts(sd, "x", n_src, (T, D), 1.0, act)
-    out["x"] = xs if shape.emulate_all_ranks else xs[0]
 
     # router and down projection
     if grid:
@@ -211,6 +220,22 @@ def generate(shape: Shape, seed=0, grid=False, send_cap=None, with_foreign=True)
     else:
         out["receiver"] = 0
 
+    # tokens: rank s draws from stream ("x", s), so a one-rank workload's own
+    # tokens are the receiver's tokens of the all-rank emulation
+    if shape.emulate_all_ranks:
+        if grid:
+            if not grid_sum_bound_ok(shape):
+                raise ValueError("exact-grid construction needs d_model * 8 * 255 < 2**24")
+            out["x"] = _store(np.stack([_grid_x(sd.rng("x", s), (T, D)) for s in range(R)]), act)
+        else:
+            out["x"] = _normal_parts(sd, "x", R, (T, D), 1.0, act)
+    else:
+        if grid and not grid_sum_bound_ok(shape):
+            raise ValueError("exact-grid construction needs d_model * 8 * 255 < 2**24")
+        out["x"] = source_tokens(shape, seed, out["receiver"], grid)
+        if shape.foreign == "routed":
+            out["sources"] = lambda s, _sh=shape, _seed=seed, _g=grid: source_tokens(_sh, _seed, s, _g)
+
     if full or shape.emulate_all_ranks:
         n_exp = E if shape.emulate_all_ranks else X
         out["w13"] = _normal_parts(sd, "w13", n_exp, (2 * H, L), L ** -0.5, act)
@@ -222,8 +247,9 @@ def generate(shape: Shape, seed=0, grid=False, send_cap=None, with_foreign=True)
     if not shape.emulate_all_ranks and with_foreign:
         if send_cap is None:
             raise ValueError("send_cap is required for one-rank workloads")
-        fid, frows = foreign_pools(shape, sd, int(send_cap), out["receiver"], out["bias"])
-        out["foreign_ids"], out["foreign_rows"] = fid, frows
+        if shape.foreign == "drawn":
+            fid, frows = foreign_pools(shape, sd, int(send_cap), out["receiver"], out["bias"])
+            out["foreign_ids"], out["foreign_rows"] = fid, frows
         if full:
             out["foreign_ret"] = foreign_returns(shape, sd, int(send_cap), out["receiver"])
     return out
