@@ -21,6 +21,8 @@
 // fp32 path: a plain per-element kernel (small layers only).
 #pragma once
 
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -313,6 +315,10 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 // the next step into the other buffer (free: every wave finished reading it
 // before the barrier that opened this step); the last substep waits for those
 // loads, passes the barrier and reads the first fragments of the next step.
+// The fragment reads are inline ds_read_b128 (so the compiler, which cannot
+// tell the two LDS buffers apart, does not make them wait for the loads in
+// flight to the other buffer); a fragment stays live until the lgkm_wait that
+// retires it, and no read is left in flight past the loop.
 // Loads move 128-byte row segments (whole L2 lines); each wave's blocks are
 // contiguous in LDS so one M0 value serves four loads through the
 // instruction's immediate offset (which also shifts the HBM address; it is
@@ -401,8 +407,12 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
   };
   Frags F[KS];
   // step kt: enters with the reads of substep 0 (F[0]) issued and step kt's
-  // tiles visible; the loads of step kt+1 go out during substeps 0..1.
-  auto step = [&](int kt) {
+  // tiles visible; the loads of step kt+1 go out during substeps 0..1.  The
+  // last step (LAST) issues neither loads nor reads for a step that does not
+  // exist, so no LDS read is in flight when the loop ends (the epilogue reuses
+  // the fragment registers).
+  auto step = [&](int kt, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS) {
@@ -411,17 +421,19 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
         for (int q = 0; q < NMMA; ++q) {
           mma1(F[ks], q);
           if (q < NF) read1(F[ks + 1], kt, ks + 1, q);
-          else if (ks * (NMMA - NF) + (q - NF) < NLOAD) load1(kt + 1, ks * (NMMA - NF) + (q - NF));
+          else if (!LAST && ks * (NMMA - NF) + (q - NF) < NLOAD) load1(kt + 1, ks * (NMMA - NF) + (q - NF));
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
         lgkm_wait<0>(F[ks].a, F[ks].b);
-        vm_wait<0>();                         // step kt+1's tiles (this lane's part)
-        lds_barrier();                        // ... every lane's; step kt's buffer is free
+        if (!LAST) {
+          vm_wait<0>();                         // step kt+1's tiles (this lane's part)
+          lds_barrier();                        // ... every lane's; step kt's buffer is free
+        }
 #pragma unroll
         for (int q = 0; q < NMMA; ++q) {
           mma1(F[ks], q);
-          if (q < NF) read1(F[0], kt + 1, 0, q);  // past the last step: a stale buffer, unused
+          if (!LAST && q < NF) read1(F[0], kt + 1, 0, q);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -433,8 +445,8 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
   lds_barrier();
 #pragma unroll
   for (int q = 0; q < NF; ++q) read1(F[0], 0, 0, q);
-  for (int kt = 0; kt < nk; ++kt) step(kt);
-  vm_wait<0>();
+  for (int kt = 0; kt + 1 < nk; ++kt) step(kt, std::integral_constant<bool, false>());
+  step(nk - 1, std::integral_constant<bool, true>());
 
   // Accumulator layout (B fragment first): lane holds row m = base + lane%32 and
   // columns n = base + 8*(v/4) + 4*(lane/32) + v%4.
