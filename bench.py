@@ -17,8 +17,8 @@ Prints ONE JSON line with, besides the contract fields:
   kernels       every kernel's average duration and roofline fraction
   cpu_baseline  the CPU oracle timed on a bounded sample of the same layer
 
-Options: --steps K --warmup W --config {2,3,4,5} --gather {fused,buffer}
---no-cpu-baseline --cpu-tokens N --seed S.  --gpus N > 1 exits: this build
+Options: --steps K --warmup W --config {2,3,4,5} --gather {fused,buffer} --streams {1,2}
+--no-cpu-baseline --cpu-tokens N --seed S.  --gpus N > 1 exits: the benchmark
 measures one GPU.
 """
 
@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--gather", choices=["fused", "buffer"], default="fused")
+    ap.add_argument("--streams", type=int, choices=[1, 2], default=2,
+                    help="2: the shared experts run on a second stream, beside the routed path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens per rank of the CPU-oracle sample (0: the whole workload)")
@@ -159,20 +161,22 @@ def main():
     del inp
     stream = torch.cuda.current_stream()
     full = sh.layer == "full"
+    side = torch.cuda.Stream() if args.streams == 2 and full else None
 
     for _ in range(args.warmup):
-        lay.run(stream)
+        lay.run(stream, side)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(args.steps):
-        lay.run(stream)
-    t1.record(stream)
+        lay.run(stream, side)
+    t1.record(stream)   # the last step's combine waited for its shared experts
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
 
-    # per-kernel pass: every library launch bracketed by HIP events on its stream
+    # per-kernel pass, all on one stream so that no two kernels share the
+    # chip: every library launch bracketed by HIP events on its stream
     binding.timing_read()
     binding.timing_enable(True)
     for _ in range(args.steps):

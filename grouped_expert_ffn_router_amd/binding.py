@@ -18,7 +18,7 @@ MOE_ACT_BF16, MOE_ACT_F32 = 0, 1
 MOE_MAX_RANKS, MOE_MAX_LOCAL = 1024, 64
 
 ENTRY_POINTS = ["moe_capacity", "moe_workspace_size", "moe_route", "moe_pack_pools", "moe_recv_waves",
-                "moe_expert_gemm", "moe_combine", "moe_drop_stats", "moe_last_error", "moe_timing_enable",
+                "moe_expert_gemm", "moe_shared_experts", "moe_combine", "moe_drop_stats", "moe_last_error", "moe_timing_enable",
                 "moe_timing_read"]
 
 
@@ -79,7 +79,8 @@ def lib():
     L.moe_pack_pools.argtypes = [DP, _P, _P, _P, _I64, _P, _P, _P, _P]
     L.moe_recv_waves.argtypes = [DP, _P, _I64, _I32, _P, _P, _P, _P, _P]
     L.moe_expert_gemm.argtypes = [DP, _I32, _P, _P, _I64, _P, _P, _P, _P, _P, _I64, _P, _P]
-    L.moe_combine.argtypes = [DP, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    L.moe_shared_experts.argtypes = [DP, _P, _P, _P, _P]
+    L.moe_combine.argtypes = [DP, _P, _I64, _P, _P, _P, _P, _P, _P, _P]
     L.moe_drop_stats.argtypes = [DP, _P, ctypes.POINTER(DropReport), _P]
     L.moe_last_error.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
@@ -162,11 +163,14 @@ def expert_gemm(dims, wave, wave_buf, recv_pools, src_stride_bytes, row_src, wav
                                  _stream(stream)))
 
 
-def combine(dims, ret_pools, ret_dst_stride_bytes, slot_of, topk_w, w_up, x, ws13, ws2, out, ws,
-            stream=None):
+def shared_experts(dims, x, ws13, ws, stream=None):
+    _check(lib().moe_shared_experts(ctypes.byref(dims), _ptr(x), _ptr(ws13), _ptr(ws), _stream(stream)))
+
+
+def combine(dims, ret_pools, ret_dst_stride_bytes, slot_of, topk_w, w_up, ws2, out, ws, stream=None):
     _check(lib().moe_combine(ctypes.byref(dims), _ptr(ret_pools), int(ret_dst_stride_bytes),
-                             _ptr(slot_of), _ptr(topk_w), _ptr(w_up), _ptr(x), _ptr(ws13), _ptr(ws2),
-                             _ptr(out), _ptr(ws), _stream(stream)))
+                             _ptr(slot_of), _ptr(topk_w), _ptr(w_up), _ptr(ws2), _ptr(out), _ptr(ws),
+                             _stream(stream)))
 
 
 def drop_stats(dims, ws, stream=None, raise_on_bad_ids=True):

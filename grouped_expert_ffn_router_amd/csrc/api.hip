@@ -281,29 +281,27 @@ hipError_t expert_gemms(const Q& q, A a1, int wave, const int32_t* row_src, cons
 }
 
 template <class T>
-hipError_t shared_and_up(const Q& q, const void* x, const void* ws13, const void* ws2, const void* w_up, T* cat,
-                         void* out, hipStream_t st) {
+hipError_t shared_gate(const Q& q, const void* x, const void* ws13, T* cat, hipStream_t st) {
   const int64_t ldc = q.L + q.S * q.HS;
   ARows<T> a1{(const T*)x, q.D, 0, nullptr, (int)q.T};
   BGateUp<T> b1{(const T*)ws13, q.D, 0, (int)q.HS, 2 * q.HS * q.D};
   ESwiGLU<T> e1{cat, ldc, 0, (int)q.L};
+  if constexpr (sizeof(T) == 2)
+    return gemm_bf16<true>("shared_gate_up", a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
+  else
+    return gemm_f32<true>("shared_gate_up", a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
+}
+
+template <class T>
+hipError_t up_and_shared_down(const Q& q, const void* ws2, const void* w_up, T* cat, void* out, hipStream_t st) {
+  const int64_t ldc = q.L + q.S * q.HS;
   ARows<T> a2{cat, ldc, 0, nullptr, (int)q.T};
   BKSeg<T> b2{(const T*)w_up, q.L, (int)q.L, (const T*)ws2, q.HS, (int)q.HS, q.D * q.HS};
   EStore<T> e2{(T*)out, q.D};
-  hipError_t r;
-  if constexpr (sizeof(T) == 2) {
-    if (q.S > 0) {
-      r = gemm_bf16<true>("shared_gate_up", a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
-      if (r != hipSuccess) return r;
-    }
+  if constexpr (sizeof(T) == 2)
     return gemm_bf16<false>("up_shared_down", a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
-  } else {
-    if (q.S > 0) {
-      r = gemm_f32<true>("shared_gate_up", a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
-      if (r != hipSuccess) return r;
-    }
+  else
     return gemm_f32<false>("up_shared_down", a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
-  }
 }
 
 }  // namespace
@@ -502,16 +500,29 @@ int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf, co
   return MOE_OK;
 }
 
+int moe_shared_experts(const moe_dims* dims, const void* x, const void* ws13, void* ws, void* stream) {
+  Q q;
+  int rc = derive(dims, &q);
+  if (rc) return rc;
+  if (q.T == 0 || q.S == 0) return MOE_OK;
+  NEED(x, "x"); NEED(ws13, "ws13"); NEED(ws, "ws");
+  const WsLayout w = layout(q);
+  hipStream_t st = (hipStream_t)stream;
+  void* cat = at<char>(ws, w.cat);
+  HIP_TRY(q.bf16 ? shared_gate<bf16_t>(q, x, ws13, (bf16_t*)cat, st) : shared_gate<float>(q, x, ws13, (float*)cat, st),
+          "moe_shared_experts gemm");
+  return MOE_OK;
+}
+
 int moe_combine(const moe_dims* dims, const void* ret_pools, int64_t ret_dst_stride_bytes, const int32_t* slot_of,
-                const float* topk_w, const void* w_up, const void* x, const void* ws13, const void* ws2, void* out,
-                void* ws, void* stream) {
+                const float* topk_w, const void* w_up, const void* ws2, void* out, void* ws, void* stream) {
   Q q;
   int rc = derive(dims, &q);
   if (rc) return rc;
   if (q.T == 0) return MOE_OK;
   NEED(ret_pools, "ret_pools"); NEED(w_up, "w_up"); NEED(out, "out"); NEED(ws, "ws");
-  NEED4(slot_of, "slot_of"); NEED4(topk_w, "topk_w"); NEED(x, "x");
-  if (q.S > 0) { NEED(ws13, "ws13"); NEED(ws2, "ws2"); }
+  NEED4(slot_of, "slot_of"); NEED4(topk_w, "topk_w");
+  if (q.S > 0) NEED(ws2, "ws2");
   if (ret_dst_stride_bytes % 16 || ret_dst_stride_bytes < q.scap * q.row_bytes)
     return fail(MOE_EALIGN, "ret_dst_stride_bytes must be a multiple of 16 and >= send_cap * L * sizeof(act)");
   const WsLayout w = layout(q);
@@ -520,8 +531,8 @@ int moe_combine(const moe_dims* dims, const void* ret_pools, int64_t ret_dst_str
   const int64_t ldc = q.L + q.S * q.HS;
   LAUNCH("combine", st, launch_combine(q.bf16 ? 0 : 1, ret_pools, ret_dst_stride_bytes, q.row_bytes, (int)q.scap, slot_of, topk_w,
                          (int)q.T, (int)q.k, (int)q.L, cat, ldc, st), "moe_combine combine");
-  HIP_TRY(q.bf16 ? shared_and_up<bf16_t>(q, x, ws13, ws2, w_up, (bf16_t*)cat, out, st)
-                 : shared_and_up<float>(q, x, ws13, ws2, w_up, (float*)cat, out, st),
+  HIP_TRY(q.bf16 ? up_and_shared_down<bf16_t>(q, ws2, w_up, (bf16_t*)cat, out, st)
+                 : up_and_shared_down<float>(q, ws2, w_up, (float*)cat, out, st),
           "moe_combine gemm");
   return MOE_OK;
 }

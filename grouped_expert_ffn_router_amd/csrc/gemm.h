@@ -4,11 +4,11 @@
 // grouped expert FFNs (row gather from the receive pools, SwiGLU pairing,
 // scatter into the return pools) and the shared experts + up-projection.
 //
-// bf16 path (gfx950): one 256-thread workgroup (4 waves, 2 x 2) per BM x BN
-// output tile; each wave owns a (BM/2) x (BN/2) sub-tile built from
+// bf16 path (gfx950): one 512-thread workgroup (8 waves, 2 x 4) per BM x BN
+// output tile; each wave owns a (BM/2) x (BN/4) sub-tile built from
 // v_mfma_f32_32x32x16_bf16.  K advances in steps of 64 through two LDS
 // buffers filled straight from HBM (16-byte global->LDS loads, each group of
-// 8 lanes reading one 128-byte row segment) one step ahead of the MFMAs.
+// 8 lanes reading one 128-byte row segment) ahead of the MFMAs.
 // LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled per row,
 // so the fragment reads run at the bank-conflict-free rate.
 // The MFMA is issued with the B fragment as its first operand, so every lane
@@ -234,10 +234,11 @@ struct EStore {
 template <int BM_, int BN_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 64;       // 2 LDS buffers of BK-deep tiles
-  static constexpr int NT = 256;                          // 4 waves, 2 x 2
-  static constexpr int WTM = BM / 2, WTN = BN / 2;        // wave sub-tile
+  static constexpr int NT = 512;                          // 8 waves (2 per SIMD), 2 x 4
+  static constexpr int WTM = BM / 2, WTN = BN / 4;        // wave sub-tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;      // 32x32 fragments per wave
-  static constexpr int LA = BM / 32, LB = BN / 32;        // 16-byte loads per lane per K step
+  static constexpr int RPW = BM / 8;                      // rows of each operand one wave loads
+  static constexpr int LA = RPW / 8, LB = RPW / 8;        // 16-byte loads per lane per K step
   static constexpr int ROW = BK * 2;                      // bytes of one LDS row (128)
   static constexpr int STAGE = (BM + BN) * ROW;           // bytes of one LDS buffer
   static_assert(BM == 256 && BN == 256, "the loader and fragment layout assume 256 x 256 tiles");
@@ -245,7 +246,7 @@ struct TileCfg {
 };
 
 // Logical tile of workgroup `bid`: XCD-contiguous ranges, M-grouped order
-// inside a group.  Returns false past the end.
+// inside a group.
 __device__ __forceinline__ void tile_of(int bid, int nb, int tiles_m, int tiles_n, int& g, int& tm, int& tn) {
   const int xcd = bid & 7, idx = bid >> 3;
   const int per = nb >> 3, rem = nb & 7;
@@ -272,10 +273,9 @@ __device__ __forceinline__ void lds_read16(bf16x8& v, uint32_t addr) {
 // the statement so that their consumers stay behind it.
 template <int N, int FM, int FN>
 __device__ __forceinline__ void lgkm_wait(bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
-  static_assert(FM == 4 && FN == 4, "fragment counts of the 256 x 256 tile");
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]),
-                 "+v"(fb[3])
+  static_assert(FM == 4 && FN == 2, "fragment counts of a 128 x 64 wave tile");
+  asm volatile("s_waitcnt lgkmcnt(%6)"
+               : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1])
                : "i"(N)
                : "memory");
 }
@@ -302,33 +302,36 @@ __device__ __forceinline__ void vm_wait() {
 // rows run 8-way conflicted and r & 7 2-way.  Rows 16 apart share it.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// grid: (groups * tiles_m * tiles_n); block: 256.  K must be a multiple of 64.
+// grid: (groups * tiles_m * tiles_n); block: 512.  K must be a multiple of 64.
 // GATEUP: N counts gate+up columns (blocks of 64) and the epilogue gets
 // (gate, up) pairs.
 //
-// Pipeline: two LDS buffers of 64-deep K steps.  A step is 4 substeps of
-// k16, each 16 MFMAs per wave on one set of fragments.  With one wave per
-// SIMD the instruction stream issues in order, so every LDS read and every
-// HBM->LDS load sits between two MFMAs (pinned by scheduling fences): a
-// stalled issue never leaves the MFMA pipe without queued work.  Substep s
-// reads the fragments of substep s+1; substeps 0 and 1 also issue the loads of
-// the next step into the other buffer (free: every wave finished reading it
-// before the barrier that opened this step); the last substep waits for those
-// loads, passes the barrier and reads the first fragments of the next step.
+// Pipeline: two LDS buffers of 64-deep K steps; 8 waves, two per SIMD, so
+// that one wave's MFMAs run while the other waits.  A step is 4 substeps of
+// k16, each 8 MFMAs per wave on one set of fragments; every LDS read and
+// every HBM->LDS load sits between two MFMAs (pinned by scheduling fences).
+// Substep s reads the fragments of substep s+1.  The last substep waits for
+// the next step's loads, passes the barrier (after which every wave is done
+// with the current step's buffer), reads the first fragments of the next
+// step and issues half of the loads of the step after next into the buffer
+// just freed; the other half goes out in the next step's first substep.  A
+// load so has most of a step (about 2000 MFMA cycles) to land.
 // The fragment reads are inline ds_read_b128 (so the compiler, which cannot
 // tell the two LDS buffers apart, does not make them wait for the loads in
 // flight to the other buffer); a fragment stays live until the lgkm_wait that
-// retires it, and no read is left in flight past the loop.
+// retires it, and every read is retired where the code passes from one step
+// variant to another (their fragment registers differ) and at the end.
 // Loads move 128-byte row segments (whole L2 lines); each wave's blocks are
 // contiguous in LDS so one M0 value serves four loads through the
 // instruction's immediate offset (which also shifts the HBM address; it is
 // subtracted from the row pointers up front).
 template <class Cfg, bool GATEUP, class A, class B, class E>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WTM = Cfg::WTM, WTN = Cfg::WTN;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, LA = Cfg::LA, LB = Cfg::LB, STAGE = Cfg::STAGE;
-  constexpr int ROW = Cfg::ROW, NLOAD = LA + LB;
+  constexpr int ROW = Cfg::ROW, RPW = Cfg::RPW, NLOAD = LA + LB, WBYTES = RPW * ROW;
+  static_assert(LA == 4 && LB == 4, "one M0 value per operand and wave");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   int g, tm, tn;
@@ -337,24 +340,24 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
   const int m0 = tm * BM, n0 = tn * BN;
   if (m0 >= M) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  // wave w owns the 8 LDS blocks (1 KB = 8 rows) w*8 .. w*8+7 of A and of B:
-  // slot d holds rows w*64 + d*8 + lane/8, lane lands at block + 16*lane.
+  // wave w owns the 4 LDS blocks (1 KB = 8 rows) w*4 .. w*4+3 of A and of B:
+  // slot d holds rows w*32 + d*8 + lane/8, lane lands at block + 16*lane.
   const int lrow = lane >> 3, lcol = lane & 7;
-  const bf16_t* pa[LA];
   int gcola[2];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) gcola[p] = (lcol ^ swz(wave * 64 + p * 8 + lrow)) * 8;
+  for (int p = 0; p < 2; ++p) gcola[p] = (lcol ^ swz(wave * RPW + p * 8 + lrow)) * 8;
+  const bf16_t* pa[LA];
 #pragma unroll
   for (int d = 0; d < LA; ++d)
-    pa[d] = a.row(g, min(m0 + wave * 64 + d * 8 + lrow, M - 1)) + gcola[d & 1] - 512 * (d & 3);
+    pa[d] = a.row(g, min(m0 + wave * RPW + d * 8 + lrow, M - 1)) + gcola[d & 1] - 512 * d;
   const bf16_t* pb[LB];
   int nb_row[LB];
 #pragma unroll
   for (int d = 0; d < LB; ++d) {
-    nb_row[d] = min(n0 + wave * 64 + d * 8 + lrow, N - 1);
-    pb[d] = b.ptr(g, nb_row[d], gcola[d & 1]) - 512 * (d & 3);
+    nb_row[d] = min(n0 + wave * RPW + d * 8 + lrow, N - 1);
+    pb[d] = b.ptr(g, nb_row[d], gcola[d & 1]) - 512 * d;
   }
   const int nk = K / BK;
 
@@ -374,27 +377,28 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
   struct Frags {
     bf16x8 a[FM], b[FN];
   };
-  constexpr int NF = FM + FN, NMMA = FM * FN, KS = BK / 16;
+  constexpr int NF = FM + FN, NMMA = FM * FN, KS = BK / 16, LH = NLOAD / 2;
+  static_assert(NF <= NMMA && LH <= NMMA && KS % 2 == 0, "one read and one load per MFMA slot at most");
   auto read1 = [&](Frags& f, int kt, int ks, int q) {
     const uint32_t st = (uint32_t)((kt & 1) * STAGE) + (uint32_t)(((ks * 2 + fhalf) ^ fswz) << 4);
     if (q < FM) lds_read16(f.a[q], fa_base + st + q * 32 * ROW);
     else lds_read16(f.b[q - FM], fb_base + st + (q - FM) * 32 * ROW);
   };
-  auto load1 = [&](int kt, int d) {  // d in [0, NLOAD)
-    const int k0 = min(kt, nk - 1) * BK;
+  auto load1 = [&](int kt, int d) {  // d in [0, NLOAD), kt < nk
+    const int k0 = kt * BK;
     char* s = smem + (kt & 1) * STAGE;
     const void* gp;
     char* lp;
     const int dd = d < LA ? d : d - LA;
     if (d < LA) {
       gp = (const void*)(pa[dd] + k0);
-      lp = s + wave * 8192 + (dd >> 2) * 4096;
+      lp = s + wave * WBYTES;
     } else {
-      gp = (const void*)(B::KSEG ? b.ptr(g, nb_row[dd], k0 + gcola[dd & 1]) - 512 * (dd & 3) : pb[dd] + k0);
-      lp = s + BM * ROW + wave * 8192 + (dd >> 2) * 4096;
+      gp = (const void*)(B::KSEG ? b.ptr(g, nb_row[dd], k0 + gcola[dd & 1]) - 512 * dd : pb[dd] + k0);
+      lp = s + BM * ROW + wave * WBYTES;
     }
     auto l3 = (__attribute__((address_space(3))) void*)lp;
-    switch (dd & 3) {
+    switch (dd) {
       case 0: __builtin_amdgcn_global_load_lds(gp, l3, 16, 0, 0); break;
       case 1: __builtin_amdgcn_global_load_lds(gp, l3, 16, 1024, 0); break;
       case 2: __builtin_amdgcn_global_load_lds(gp, l3, 16, 2048, 0); break;
@@ -405,48 +409,72 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
     const int i = q / FN, j = q % FN;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
-  Frags F[KS];
-  // step kt: enters with the reads of substep 0 (F[0]) issued and step kt's
-  // tiles visible; the loads of step kt+1 go out during substeps 0..1.  The
-  // last step (LAST) issues neither loads nor reads for a step that does not
-  // exist, so no LDS read is in flight when the loop ends (the epilogue reuses
-  // the fragment registers).
-  auto step = [&](int kt, auto last_tag) {
-    constexpr bool LAST = decltype(last_tag)::value;
+  Frags F[2];  // substep ks computes on F[ks & 1] while F[(ks + 1) & 1] is read
+  // One K step.  MODE 0: issues loads [0, LH) of step kt+2 after its barrier;
+  // 1: no new loads; 2: the last step (no barrier, no next reads).  HALF:
+  // the previous step left loads [LH, NLOAD) of step kt+1 to substep 0.
+  auto step = [&](int kt, auto mode_tag, auto half_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    constexpr bool HALF = decltype(half_tag)::value;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      Frags& cur = F[ks & 1];
+      Frags& nxt = F[(ks + 1) & 1];
+      lgkm_wait<0>(cur.a, cur.b);
       if (ks + 1 < KS) {
-        lgkm_wait<0>(F[ks].a, F[ks].b);
 #pragma unroll
         for (int q = 0; q < NMMA; ++q) {
-          mma1(F[ks], q);
-          if (q < NF) read1(F[ks + 1], kt, ks + 1, q);
-          else if (!LAST && ks * (NMMA - NF) + (q - NF) < NLOAD) load1(kt + 1, ks * (NMMA - NF) + (q - NF));
+          mma1(cur, q);
+          if (q < NF) read1(nxt, kt, ks + 1, q);
+          if (HALF && ks == 0 && q < NLOAD - LH) load1(kt + 1, LH + q);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        lgkm_wait<0>(F[ks].a, F[ks].b);
-        if (!LAST) {
-          vm_wait<0>();                         // step kt+1's tiles (this lane's part)
-          lds_barrier();                        // ... every lane's; step kt's buffer is free
+        if (MODE != 2) {
+          vm_wait<0>();   // step kt+1's tiles (this lane's part)
+          lds_barrier();  // ... every lane's; every wave is done with step kt's buffer
         }
 #pragma unroll
         for (int q = 0; q < NMMA; ++q) {
-          mma1(F[ks], q);
-          if (!LAST && q < NF) read1(F[0], kt + 1, 0, q);
+          mma1(cur, q);
+          if (MODE != 2 && q < NF) read1(nxt, kt + 1, 0, q);
+          if (MODE == 0 && q < LH) load1(kt + 2, q);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   };
+  using Loads = std::integral_constant<int, 0>;
+  using NoLoads = std::integral_constant<int, 1>;
+  using Last = std::integral_constant<int, 2>;
+  using Half = std::true_type;
+  using Whole = std::false_type;
 #pragma unroll
   for (int d = 0; d < NLOAD; ++d) load1(0, d);
   vm_wait<0>();
   lds_barrier();
+  if (nk > 1) {
+#pragma unroll
+    for (int d = 0; d < NLOAD; ++d) load1(1, d);
+  }
 #pragma unroll
   for (int q = 0; q < NF; ++q) read1(F[0], 0, 0, q);
-  for (int kt = 0; kt + 1 < nk; ++kt) step(kt, std::integral_constant<bool, false>());
-  step(nk - 1, std::integral_constant<bool, true>());
+  lgkm_wait<0>(F[0].a, F[0].b);
+  if (nk >= 3) {
+    step(0, Loads(), Whole());
+    lgkm_wait<0>(F[0].a, F[0].b);
+    for (int kt = 1; kt + 2 < nk; ++kt) step(kt, Loads(), Half());
+    lgkm_wait<0>(F[0].a, F[0].b);
+    step(nk - 2, NoLoads(), Half());
+    lgkm_wait<0>(F[0].a, F[0].b);
+    step(nk - 1, Last(), Whole());
+  } else if (nk == 2) {
+    step(0, NoLoads(), Whole());
+    lgkm_wait<0>(F[0].a, F[0].b);
+    step(1, Last(), Whole());
+  } else {
+    step(0, Last(), Whole());
+  }
 
   // Accumulator layout (B fragment first): lane holds row m = base + lane%32 and
   // columns n = base + 8*(v/4) + 4*(lane/32) + v%4.
@@ -456,6 +484,7 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
     if (m >= M) continue;
     const auto rc = e.row(g, m);
     if constexpr (GATEUP) {
+      static_assert(FN % 2 == 0, "gate and up fragments come in pairs");
 #pragma unroll
       for (int j = 0; j < FN; j += 2) {
 #pragma unroll

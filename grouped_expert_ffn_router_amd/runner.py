@@ -101,6 +101,7 @@ class OneRankLayer:
             self.ret_send = torch.zeros((R, self.scap, L), dtype=act, device=dev)
             self.ret_recv = upload(inp["foreign_ret"], dev)
             self.out = torch.empty((T, D), dtype=act, device=dev)
+            self._ev_go, self._ev_shared = torch.cuda.Event(), torch.cuda.Event()
         if "sources" in inp:
             self._route_other_ranks(inp["sources"])
 
@@ -147,20 +148,40 @@ class OneRankLayer:
                       self.wave_count[w], self.w13, self.w2, self.ret_send, self.scap * self.shape.latent * self.esize,
                       self.ws, stream)
 
+    def shared(self, stream=None):
+        B.shared_experts(self.dims, self.x, self.ws13, self.ws, stream)
+
     def combine(self, stream=None):
         # self-block of the return exchange
         self.ret_recv[self.rank].copy_(self.ret_send[self.rank])
         B.combine(self.dims, self.ret_recv, self.scap * self.shape.latent * self.esize, self.slot_of, self.w,
-                  self.w_up, self.x, self.ws13, self.ws2, self.out, self.ws, stream)
+                  self.w_up, self.ws2, self.out, self.ws, stream)
 
-    def run(self, stream=None):
-        self.dispatch(stream)
-        for w in range(self.shape.waves):
-            self.receive_wave(w, stream)
+    def run(self, stream=None, side=None):
+        """One batch on `stream` (torch's current stream if None).  With `side`,
+        a second stream, the shared experts run there, concurrently with the
+        routed path: they start once everything queued before on `stream`
+        (the previous batch's combine, which reads their output) is done,
+        and the combine waits for them."""
+        main = stream if stream is not None else torch.cuda.current_stream()
+        with torch.cuda.stream(main):
             if self.full:
-                self.expert_wave(w, stream)
-        if self.full:
-            self.combine(stream)
+                if side is not None:
+                    self._ev_go.record(main)
+                    side.wait_event(self._ev_go)
+                    self.shared(side)
+                    self._ev_shared.record(side)
+                else:
+                    self.shared(main)
+            self.dispatch(main)
+            for w in range(self.shape.waves):
+                self.receive_wave(w, main)
+                if self.full:
+                    self.expert_wave(w, main)
+            if self.full:
+                if side is not None:
+                    main.wait_event(self._ev_shared)
+                self.combine(main)
 
     def drop_report(self, stream=None):
         return B.drop_stats(self.dims, self.ws, stream, raise_on_bad_ids=False).as_dict()
@@ -231,8 +252,9 @@ class AllRanksLayer:
         for s in range(R):
             d = self.dims[s]
             ret_view = self.ret[0, s]                    # rows from receiver d at + d * R * scap * L
-            B.combine(d, ret_view, R * self.scap * L * esize, self.slot_of[s], self.w[s], self.w_up, self.x[s],
-                      self.ws13, self.ws2, self.out[s], self.ws[s], stream)
+            B.shared_experts(d, self.x[s], self.ws13, self.ws[s], stream)
+            B.combine(d, ret_view, R * self.scap * L * esize, self.slot_of[s], self.w[s], self.w_up, self.ws2,
+                      self.out[s], self.ws[s], stream)
 
     def drop_reports(self, stream=None):
         return [B.drop_stats(self.dims[r], self.ws[r], stream, raise_on_bad_ids=False).as_dict()

@@ -165,19 +165,30 @@ int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf,
                     const int32_t* wave_count, const void* w13, const void* w2,
                     void* ret_pools, int64_t ret_src_stride_bytes, void* ws, void* stream);
 
-/* Weighted combine, up-projection and shared experts (section 二: the
- * routed output is projected back to model width before merging with the
- * shared path; section 四: shared experts see every token, so a dropped
- * assignment contributes nothing but the token is not lost).
+/* Shared experts (section 二: 2 always-on experts beside the routed ones;
+ * section 四: they see every token).  For every token t and shared expert j,
+ * h_s[t][j] = act(silu(x_t . Wg_j^T) * (x_t . Wu_j^T)), kept in `ws` for the
+ * moe_combine call of the same batch.  It reads nothing the routed path
+ * writes, so it may run on another stream, concurrently with moe_route ..
+ * moe_expert_gemm of the same batch, provided it completes before that
+ * batch's moe_combine starts and starts after the previous batch's
+ * moe_combine on the same `ws` has completed.  With S == 0 it does nothing.
+ *   x [T][D] act;  ws13 [S][2HS][D] act (HS gate rows then HS up rows) */
+int moe_shared_experts(const moe_dims* dims, const void* x, const void* ws13, void* ws, void* stream);
+
+/* Weighted combine and up-projection, merged with the shared experts
+ * (section 二: the routed output is projected back to model width before
+ * merging with the shared path; section 四: a dropped assignment
+ * contributes nothing but the token is not lost).
  *   c_t  = act(sum_i topk_w[t][i] * ret(slot_of[t][i]))   (slot -1 adds 0)
- *   out  = act(c . U^T + sum_j act(silu(x . Wg_j^T) * (x . Wu_j^T)) . W2_j^T)
+ *   out  = act(c . U^T + sum_j h_s[t][j] . W2_j^T)
+ * with h_s as left in `ws` by moe_shared_experts (required first when S > 0).
  *   ret_pools       row returned for slot d*send_cap+s at ret_pools +
  *                   d * ret_dst_stride_bytes + s * L * sizeof(act)
- *   w_up  [D][L] act;  ws13 [S][2HS][D] act (HS gate rows then HS up rows);
- *   ws2   [S][D][HS] act;  x [T][D];  out [T][D] act output */
+ *   w_up  [D][L] act;  ws2 [S][D][HS] act;  out [T][D] act output */
 int moe_combine(const moe_dims* dims, const void* ret_pools, int64_t ret_dst_stride_bytes,
-                const int32_t* slot_of, const float* topk_w, const void* w_up, const void* x,
-                const void* ws13, const void* ws2, void* out, void* ws, void* stream);
+                const int32_t* slot_of, const float* topk_w, const void* w_up, const void* ws2,
+                void* out, void* ws, void* stream);
 
 /* Copy the drop ledger held in `ws` to host memory (section 二: drops are
  * reported separately for the send and the receive side).  Synchronises

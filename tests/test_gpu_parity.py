@@ -228,8 +228,17 @@ def test_one_rank_full_size(runner, cfg):
             drawn = dict(zip(range(sh.n_ranks), ex.map(inp["sources"], range(sh.n_ranks))))
         inp["sources"] = drawn.__getitem__
     lay = runner.OneRankLayer(sh, inp, gather="fused")
-    lay.run()
+    # the benchmark's launch configuration: shared experts on a second stream
+    side = torch.cuda.Stream() if sh.layer == "full" else None
+    lay.run(side=side)
     torch.cuda.synchronize()
+    if side is not None:
+        # same bytes as with everything on one stream
+        out2 = host(lay.out)
+        lay.run()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(lay.out).view(np.uint8), out2.view(np.uint8)), "two streams vs one"
+        del out2
     rep = lay.drop_report()
     r = inp["receiver"]
     oin = dict(inp)
