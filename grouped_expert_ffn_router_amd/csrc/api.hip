@@ -166,7 +166,7 @@ int derive(const moe_dims* d, Q* q) {
 }
 
 struct WsLayout {
-  size_t ctr, s_cc, s_cb, s_lr, r_cc, r_cb, r_j, r_lr, r_rank, logits, h, cat, total;
+  size_t ctr, s_cc, s_cb, s_lr, r_cc, r_cb, r_j, r_lr, r_rank, logits, h, cat, part, total;
   int nch_s, nch_r;
 };
 
@@ -192,6 +192,7 @@ WsLayout layout(const Q& q) {
   w.logits = take((size_t)q.T * q.E * 4);
   w.h = take((size_t)q.WX * q.rcap * q.H * q.esize);
   w.cat = take((size_t)q.T * (q.L + q.S * q.HS) * q.esize);
+  w.part = take(q.bf16 ? (size_t)PART_SLOTS * PART_FLOATS * sizeof(float) : 0);  // tail-split partial tiles
   w.total = off;
   return w;
 }
@@ -226,15 +227,51 @@ P* at(void* ws, size_t off) { return (P*)((char*)ws + off); }
 
 // ---------------------------------------------------------------- GEMM runners
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PART_SLOTS;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = PART_SLOTS;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// bf16 GEMM launch.  part: PART_SLOTS partial tiles for the tail split, or
+// NULL (no split: launches that may run beside others on the same workspace).
+// rows_fixed: every group has max_rows rows, so the split is decided here and
+// the fixup kernel launched only when there is a tail to finish.
 template <bool GATEUP, class A, class B, class E>
-hipError_t gemm_bf16(const char* name, A a, B b, E e, int N, int K, int64_t max_rows, int groups, hipStream_t st) {
+hipError_t gemm_bf16(const char* name, const char* fixup_name, A a, B b, E e, int N, int K, int64_t max_rows,
+                     bool rows_fixed, int groups, float* part, hipStream_t st) {
   using Cfg = TileCfg<256, 256>;
   if (N <= 0 || max_rows <= 0 || groups <= 0) return hipSuccess;
-  KernelTimer kt(name, st);
+  const int P = cu_count() < PART_SLOTS ? cu_count() : PART_SLOTS;
   const int64_t tiles_m = ceil_div(max_rows, Cfg::BM), tiles_n = ceil_div(N, Cfg::BN);
-  const int64_t nb = groups * tiles_m * tiles_n;
-  hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, GATEUP, A, B, E>), dim3((unsigned)nb), dim3(Cfg::NT), 0, st, a, b, e, N,
-                     K, (int)tiles_m, (int)tiles_n);
+  const int64_t max_tiles = groups * tiles_m * tiles_n;
+  const int nk = K / Cfg::BK;
+  // no tile count gives a tail split worth taking at this K: no partials
+  const int smax = nk / KSPLIT_MIN;
+  bool split = part != nullptr && smax >= 2 && nk - nk / smax >= KSPLIT_GAIN;
+  if (split && rows_fixed) {  // the device-side plan, for a tile count known here
+    const int64_t r = max_tiles % P;
+    const int64_t parts = r > 0 ? (P / r < nk / KSPLIT_MIN ? P / r : nk / KSPLIT_MIN) : 0;
+    split = r > 0 && 2 * r <= P && parts >= 2 && nk - nk / parts >= KSPLIT_GAIN;
+  }
+  {
+    KernelTimer kt(name, st);
+    hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, GATEUP, A, B, E>), dim3((unsigned)gemm_grid(max_tiles, P)), dim3(Cfg::NT), 0,
+                       st, a, b, e, N, K, groups, (int)tiles_n, P, split ? part : nullptr);
+    hipError_t r = hipGetLastError();
+    if (r != hipSuccess) return r;
+  }
+  if (!split) return hipSuccess;
+  KernelTimer kt(fixup_name, st);
+  hipLaunchKernelGGL((gemm_bf16_fixup<Cfg, GATEUP, A, E>), dim3(2048u), dim3(64), 0, st, a, e,
+                     N, K, groups, (int)tiles_n, P, (const float*)part);
   return hipGetLastError();
 }
 
@@ -251,17 +288,19 @@ hipError_t gemm_f32(const char* name, A a, B b, E e, int N, int K, int64_t max_r
 // route GEMM: logits | z = x . [W_r ; W_d]^T
 template <class T>
 hipError_t route_gemm(const Q& q, const void* x, const void* wr, const void* wd, const float* bias, int brt,
-                      float* logits, void* z, hipStream_t st) {
+                      float* logits, void* z, float* part, hipStream_t st) {
   ARows<T> a{(const T*)x, q.D, 0, nullptr, (int)q.T};
   BTwo<T> b{(const T*)wr, (const T*)wd, (int)q.E, q.D};
   ERouteDown<T> e{logits, (T*)z, bias, (int)q.E, (int)q.L, brt};
-  if constexpr (sizeof(T) == 2) return gemm_bf16<false>("route_gemm", a, b, e, (int)(q.E + q.L), (int)q.D, q.T, 1, st);
+  if constexpr (sizeof(T) == 2)
+    return gemm_bf16<false>("route_gemm", "route_fixup", a, b, e, (int)(q.E + q.L), (int)q.D, q.T, true, 1, part, st);
   else return gemm_f32<false>("route_gemm", a, b, e, (int)(q.E + q.L), (int)q.D, q.T, 1, st);
 }
 
 template <class T, class A>
 hipError_t expert_gemms(const Q& q, A a1, int wave, const int32_t* row_src, const int32_t* wave_count,
-                        const void* w13, const void* w2, void* ret, int64_t ret_src_stride, T* h, hipStream_t st) {
+                        const void* w13, const void* w2, void* ret, int64_t ret_src_stride, T* h, float* part,
+                        hipStream_t st) {
   const int64_t x0 = (int64_t)wave * q.WX;
   BGateUp<T> b1{(const T*)w13 + x0 * 2 * q.H * q.L, q.L, 2 * q.H * q.L, (int)q.H, 0};
   ESwiGLU<T> e1{h, q.H, q.rcap * q.H, 0};
@@ -270,9 +309,11 @@ hipError_t expert_gemms(const Q& q, A a1, int wave, const int32_t* row_src, cons
   EScatter<T> e2{(char*)ret, ret_src_stride, q.row_bytes, (int)q.scap, row_src, q.rcap};
   hipError_t r;
   if constexpr (sizeof(T) == 2) {
-    r = gemm_bf16<true>("expert_gate_up", a1, b1, e1, (int)(2 * q.H), (int)q.L, q.rcap, (int)q.WX, st);
+    r = gemm_bf16<true>("expert_gate_up", "gate_up_fixup", a1, b1, e1, (int)(2 * q.H), (int)q.L, q.rcap, false,
+                        (int)q.WX, part, st);
     if (r != hipSuccess) return r;
-    return gemm_bf16<false>("expert_down", a2, b2, e2, (int)q.L, (int)q.H, q.rcap, (int)q.WX, st);
+    return gemm_bf16<false>("expert_down", "down_fixup", a2, b2, e2, (int)q.L, (int)q.H, q.rcap, false, (int)q.WX,
+                            part, st);
   } else {
     r = gemm_f32<true>("expert_gate_up", a1, b1, e1, (int)(2 * q.H), (int)q.L, q.rcap, (int)q.WX, st);
     if (r != hipSuccess) return r;
@@ -287,19 +328,21 @@ hipError_t shared_gate(const Q& q, const void* x, const void* ws13, T* cat, hipS
   BGateUp<T> b1{(const T*)ws13, q.D, 0, (int)q.HS, 2 * q.HS * q.D};
   ESwiGLU<T> e1{cat, ldc, 0, (int)q.L};
   if constexpr (sizeof(T) == 2)
-    return gemm_bf16<true>("shared_gate_up", a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
+    return gemm_bf16<true>("shared_gate_up", "", a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, true, 1, nullptr,
+                           st);  // may run beside the routed path: no shared partial area
   else
     return gemm_f32<true>("shared_gate_up", a1, b1, e1, (int)(2 * q.S * q.HS), (int)q.D, q.T, 1, st);
 }
 
 template <class T>
-hipError_t up_and_shared_down(const Q& q, const void* ws2, const void* w_up, T* cat, void* out, hipStream_t st) {
+hipError_t up_and_shared_down(const Q& q, const void* ws2, const void* w_up, T* cat, void* out, float* part,
+                              hipStream_t st) {
   const int64_t ldc = q.L + q.S * q.HS;
   ARows<T> a2{cat, ldc, 0, nullptr, (int)q.T};
   BKSeg<T> b2{(const T*)w_up, q.L, (int)q.L, (const T*)ws2, q.HS, (int)q.HS, q.D * q.HS};
   EStore<T> e2{(T*)out, q.D};
   if constexpr (sizeof(T) == 2)
-    return gemm_bf16<false>("up_shared_down", a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
+    return gemm_bf16<false>("up_shared_down", "up_fixup", a2, b2, e2, (int)q.D, (int)ldc, q.T, true, 1, part, st);
   else
     return gemm_f32<false>("up_shared_down", a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
 }
@@ -393,8 +436,8 @@ int moe_route(const moe_dims* dims, const void* x, const void* w_router, const v
   const WsLayout w = layout(q);
   hipStream_t st = (hipStream_t)stream;
   float* lg = logits ? logits : at<float>(ws, w.logits);
-  HIP_TRY(q.bf16 ? route_gemm<bf16_t>(q, x, w_router, w_down, bias, bias_row_tokens, lg, z, st)
-                 : route_gemm<float>(q, x, w_router, w_down, bias, bias_row_tokens, lg, z, st),
+  HIP_TRY(q.bf16 ? route_gemm<bf16_t>(q, x, w_router, w_down, bias, bias_row_tokens, lg, z, at<float>(ws, w.part), st)
+                 : route_gemm<float>(q, x, w_router, w_down, bias, bias_row_tokens, lg, z, nullptr, st),
           "moe_route gemm");
   LAUNCH("select_topk", st, launch_select_topk(lg, (int)q.T, (int)q.E, (int)q.k, topk_idx, topk_w, st), "moe_route select");
   return MOE_OK;
@@ -474,23 +517,24 @@ int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf, co
   const WsLayout w = layout(q);
   hipStream_t st = (hipStream_t)stream;
   hipError_t r;
+  float* part = at<float>(ws, w.part);
   if (q.bf16) {
     bf16_t* h = at<bf16_t>(ws, w.h);
     if (wave_buf) {
       ARows<bf16_t> a{(const bf16_t*)wave_buf, q.L, q.rcap * q.L, wave_count, 0};
-      r = expert_gemms<bf16_t>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, st);
+      r = expert_gemms<bf16_t>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, part, st);
     } else {
       AGather<bf16_t> a{(const char*)recv_pools, src_stride_bytes, q.prow, (int)q.scap, row_src, q.rcap, wave_count};
-      r = expert_gemms<bf16_t>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, st);
+      r = expert_gemms<bf16_t>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, part, st);
     }
   } else {
     float* h = at<float>(ws, w.h);
     if (wave_buf) {
       ARows<float> a{(const float*)wave_buf, q.L, q.rcap * q.L, wave_count, 0};
-      r = expert_gemms<float>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, st);
+      r = expert_gemms<float>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, part, st);
     } else {
       AGather<float> a{(const char*)recv_pools, src_stride_bytes, q.prow, (int)q.scap, row_src, q.rcap, wave_count};
-      r = expert_gemms<float>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, st);
+      r = expert_gemms<float>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, part, st);
     }
   }
   HIP_TRY(r, "moe_expert_gemm gemm");
@@ -531,8 +575,8 @@ int moe_combine(const moe_dims* dims, const void* ret_pools, int64_t ret_dst_str
   const int64_t ldc = q.L + q.S * q.HS;
   LAUNCH("combine", st, launch_combine(q.bf16 ? 0 : 1, ret_pools, ret_dst_stride_bytes, q.row_bytes, (int)q.scap, slot_of, topk_w,
                          (int)q.T, (int)q.k, (int)q.L, cat, ldc, st), "moe_combine combine");
-  HIP_TRY(q.bf16 ? up_and_shared_down<bf16_t>(q, ws2, w_up, (bf16_t*)cat, out, st)
-                 : up_and_shared_down<float>(q, ws2, w_up, (float*)cat, out, st),
+  HIP_TRY(q.bf16 ? up_and_shared_down<bf16_t>(q, ws2, w_up, (bf16_t*)cat, out, at<float>(ws, w.part), st)
+                 : up_and_shared_down<float>(q, ws2, w_up, (float*)cat, out, nullptr, st),
           "moe_combine gemm");
   return MOE_OK;
 }

@@ -245,23 +245,88 @@ struct TileCfg {
   static_assert(2 * STAGE <= 160 * 1024, "LDS budget of one workgroup");
 };
 
-// Logical tile of workgroup `bid`: XCD-contiguous ranges, M-grouped order
-// inside a group.
-__device__ __forceinline__ void tile_of(int bid, int nb, int tiles_m, int tiles_n, int& g, int& tm, int& tn) {
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  const int logical = xcd * per + min(xcd, rem) + idx;
-  const int tpg = tiles_m * tiles_n;
-  g = logical / tpg;
-  const int r = logical - g * tpg;
+// ---- work assignment
+// The output tiles that exist (rows(g) of each group, so a count read on the
+// device) are numbered group by group, M-grouped (GROUP_M tile rows at a
+// time) inside a group.  With P workgroups running at once, T tiles take
+// ceil(T / P) rounds; when the last round would hold only r <= P/2 tiles,
+// those r tiles are split along K into s parts each (s * r <= P, at least
+// KSPLIT_MIN steps per part) that run side by side as that round, each
+// writing an fp32 partial tile; a second kernel adds the parts in part order
+// and applies the epilogue.  The split is taken only where it shortens the
+// tail by KSPLIT_GAIN steps or more: that kernel and the partial traffic cost
+// about as much as a dozen K steps of a tile.  The other T - r tiles are dealt to the XCDs
+// (workgroups go round-robin to the 8 XCDs) in contiguous ranges, so each
+// XCD's L2 sees neighbouring tiles; the tail parts come after them.
+
+constexpr int KSPLIT_MIN = 4;    // K steps of one tail part, at least
+constexpr int KSPLIT_GAIN = 24;  // K steps a split must take off the tail, at least
+constexpr int PART_SLOTS = 256;  // partial tiles one launch may write
+
+struct TailPlan {
+  int total, tail, parts;  // tiles, tail tiles (r), parts per tail tile (s)
+};
+
+template <class A>
+__host__ __device__ __forceinline__ TailPlan tail_plan(const A& a, int groups, int tiles_n, int nk, int P, bool can_split) {
+  TailPlan t{0, 0, 0};
+  for (int g = 0; g < groups; ++g) t.total += (a.rows(g) + 255) / 256 * tiles_n;
+  const int r = t.total % P;
+  if (can_split && r > 0 && 2 * r <= P) {
+    const int s = P / r < nk / KSPLIT_MIN ? P / r : nk / KSPLIT_MIN;
+    if (s >= 2 && nk - nk / s >= KSPLIT_GAIN) {
+      t.tail = r;
+      t.parts = s;
+    }
+  }
+  return t;
+}
+
+// Tile number t -> (group, tile row, tile column).
+template <class A>
+__host__ __device__ __forceinline__ void tile_coords(const A& a, int groups, int tiles_n, int t, int& g, int& tm, int& tn) {
+  int mt = 0;
+  for (g = 0; g < groups; ++g) {
+    mt = (a.rows(g) + 255) / 256;
+    if (t < mt * tiles_n) break;
+    t -= mt * tiles_n;
+  }
   constexpr int GROUP_M = 8;
   const int width = GROUP_M * tiles_n;
-  const int gid = r / width, first_m = gid * GROUP_M;
-  const int gsz = min(tiles_m - first_m, GROUP_M);
-  const int rr = r - gid * width;
+  const int gid = t / width, first_m = gid * GROUP_M;
+  const int gsz = mt - first_m < GROUP_M ? mt - first_m : GROUP_M;
+  const int rr = t - gid * width;
   tm = first_m + rr % gsz;
   tn = rr / gsz;
 }
+
+// Work of workgroup `bid`: tile t and K steps [kb, ke); slot >= 0 names the
+// partial this tail part writes.  False: nothing to do.
+__host__ __device__ __forceinline__ bool block_work(const TailPlan& p, int nk, int bid, int& t, int& kb, int& ke, int& slot) {
+  const int D = p.total - p.tail;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int per = D >> 3, rem = D & 7;
+  const int len = per + (xcd < rem ? 1 : 0), maxlen = per + (rem ? 1 : 0);
+  kb = 0;
+  ke = nk;
+  slot = -1;
+  if (idx < len) {
+    t = xcd * per + (xcd < rem ? xcd : rem) + idx;
+    return true;
+  }
+  if (idx < maxlen) return false;
+  const int q = (idx - maxlen) * 8 + xcd;
+  if (q >= p.tail * p.parts) return false;
+  t = D + q / p.parts;
+  const int part = q % p.parts;
+  kb = part * nk / p.parts;
+  ke = (part + 1) * nk / p.parts;
+  slot = q;
+  return true;
+}
+
+// Workgroups a launch needs for at most max_tiles tiles (host side).
+inline int64_t gemm_grid(int64_t max_tiles, int P) { return 8 * ((max_tiles + 7) / 8 + (P + 7) / 8); }
 
 // 16-byte LDS read at byte address `addr`, issued as inline assembly: the
 // result must be awaited with lgkm_wait before use.
@@ -302,7 +367,6 @@ __device__ __forceinline__ void vm_wait() {
 // rows run 8-way conflicted and r & 7 2-way.  Rows 16 apart share it.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// grid: (groups * tiles_m * tiles_n); block: 512.  K must be a multiple of 64.
 // GATEUP: N counts gate+up columns (blocks of 64) and the epilogue gets
 // (gate, up) pairs.
 //
@@ -325,20 +389,70 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 // contiguous in LDS so one M0 value serves four loads through the
 // instruction's immediate offset (which also shifts the HBM address; it is
 // subtracted from the row pointers up front).
+// Epilogue of 4 columns per fragment of one output row (context rc), columns
+// nbase + j*32 + q*8 + fhalf*4 .. +3 for fragment j.  Accumulator layout (B
+// fragment first): lane holds row m = base + lane%32 and columns
+// n = base + 8*(v/4) + 4*(lane/32) + v%4 of a fragment.
+template <bool GATEUP, int FN, class E, class Row>
+__device__ __forceinline__ void epilogue_q(const E& e, const Row& rc, int nbase, int N, int fhalf, int q,
+                                           const float (&v)[FN][4]) {
+  if constexpr (GATEUP) {
+    static_assert(FN % 2 == 0, "gate and up fragments come in pairs");
+#pragma unroll
+    for (int j = 0; j < FN; j += 2) {
+      const int n = nbase + j * 32 + q * 8 + fhalf * 4;  // gate column (n % 64 < 32)
+      if (n < N) e.store4_pair(rc, (n >> 6) * 32 + (n & 31), v[j], v[j + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = nbase + j * 32 + q * 8 + fhalf * 4;
+      if (n < N) e.store4(rc, n, N, v[j]);
+    }
+  }
+}
+
+// Epilogue of fragment row i of a wave (one output row m per lane pair).
+template <bool GATEUP, int FN, class E>
+__device__ __forceinline__ void epilogue_row(const E& e, int g, int m, int M, int nbase, int N, int fhalf,
+                                             const f32x16 (&accr)[FN]) {
+  if (m >= M) return;
+  const auto rc = e.row(g, m);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v[FN][4];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[j][t] = accr[j][q * 4 + t];
+    epilogue_q<GATEUP, FN>(e, rc, nbase, N, fhalf, q, v);
+  }
+}
+
+// Partial tile layout: float4 chunk c (0..31, = (i*FN + j)*4 + v/4) of thread
+// tid at float offset (c * 512 + tid) * 4 of the slot (coalesced).
+constexpr int PART_FLOATS = 256 * 256;
+
+// grid: gemm_grid(groups * ceil(max_rows / 256) * tiles_n, P); block: 512.
+// K must be a multiple of 64.  part: PART_SLOTS partial tiles, or NULL (no
+// tail split).
 template <class Cfg, bool GATEUP, class A, class B, class E>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
+gemm_bf16_mfma(A a, B b, E e, int N, int K, int groups, int tiles_n, int P, float* part) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WTM = Cfg::WTM, WTN = Cfg::WTN;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, LA = Cfg::LA, LB = Cfg::LB, STAGE = Cfg::STAGE;
   constexpr int ROW = Cfg::ROW, RPW = Cfg::RPW, NLOAD = LA + LB, WBYTES = RPW * ROW;
   static_assert(LA == 4 && LB == 4, "one M0 value per operand and wave");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
+  const int nk = K / BK;
+  const TailPlan plan = tail_plan(a, groups, tiles_n, nk, P, part != nullptr);
+  int t, kb, ke, slot;
+  if (!block_work(plan, nk, blockIdx.x, t, kb, ke, slot)) return;
   int g, tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, g, tm, tn);
+  tile_coords(a, groups, tiles_n, t, g, tm, tn);
   const int M = a.rows(g);
   const int m0 = tm * BM, n0 = tn * BN;
-  if (m0 >= M) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
 
@@ -359,7 +473,6 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
     nb_row[d] = min(n0 + wave * RPW + d * 8 + lrow, N - 1);
     pb[d] = b.ptr(g, nb_row[d], gcola[d & 1]) - 512 * d;
   }
-  const int nk = K / BK;
 
   const int frow = lane & 31, fhalf = lane >> 5;
   const int fswz = swz(frow);
@@ -449,73 +562,97 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int tiles_m, int tiles_n) {
   using Last = std::integral_constant<int, 2>;
   using Half = std::true_type;
   using Whole = std::false_type;
+  // K steps [kb, ke): a whole tile, or one part of a tail tile
+  const int ns = ke - kb;
 #pragma unroll
-  for (int d = 0; d < NLOAD; ++d) load1(0, d);
+  for (int d = 0; d < NLOAD; ++d) load1(kb, d);
   vm_wait<0>();
   lds_barrier();
-  if (nk > 1) {
+  if (ns > 1) {
 #pragma unroll
-    for (int d = 0; d < NLOAD; ++d) load1(1, d);
+    for (int d = 0; d < NLOAD; ++d) load1(kb + 1, d);
   }
 #pragma unroll
-  for (int q = 0; q < NF; ++q) read1(F[0], 0, 0, q);
+  for (int q = 0; q < NF; ++q) read1(F[0], kb, 0, q);
   lgkm_wait<0>(F[0].a, F[0].b);
-  if (nk >= 3) {
-    step(0, Loads(), Whole());
+  if (ns >= 3) {
+    step(kb, Loads(), Whole());
     lgkm_wait<0>(F[0].a, F[0].b);
-    for (int kt = 1; kt + 2 < nk; ++kt) step(kt, Loads(), Half());
+    for (int kt = kb + 1; kt + 2 < ke; ++kt) step(kt, Loads(), Half());
     lgkm_wait<0>(F[0].a, F[0].b);
-    step(nk - 2, NoLoads(), Half());
+    step(ke - 2, NoLoads(), Half());
     lgkm_wait<0>(F[0].a, F[0].b);
-    step(nk - 1, Last(), Whole());
-  } else if (nk == 2) {
-    step(0, NoLoads(), Whole());
+    step(ke - 1, Last(), Whole());
+  } else if (ns == 2) {
+    step(kb, NoLoads(), Whole());
     lgkm_wait<0>(F[0].a, F[0].b);
-    step(1, Last(), Whole());
+    step(kb + 1, Last(), Whole());
   } else {
-    step(0, Last(), Whole());
+    step(kb, Last(), Whole());
   }
 
-  // Accumulator layout (B fragment first): lane holds row m = base + lane%32 and
-  // columns n = base + 8*(v/4) + 4*(lane/32) + v%4.
+  if (slot >= 0) {  // one part of a tail tile: fp32 partial, finished by gemm_bf16_fixup
+    float4* dst = (float4*)(part + (int64_t)slot * PART_FLOATS);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + frow;
-    if (m >= M) continue;
-    const auto rc = e.row(g, m);
-    if constexpr (GATEUP) {
-      static_assert(FN % 2 == 0, "gate and up fragments come in pairs");
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; j += 2) {
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WTN + j * 32 + q * 8 + fhalf * 4;  // gate column (n % 64 < 32)
-          if (n < N) {
-            float gv[4], uv[4];
+        for (int v = 0; v < 4; ++v)
+          dst[((i * FN + j) * 4 + v) * 512 + tid] =
+              make_float4(acc[i][j][v * 4], acc[i][j][v * 4 + 1], acc[i][j][v * 4 + 2], acc[i][j][v * 4 + 3]);
+    return;
+  }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              gv[t] = acc[i][j][q * 4 + t];
-              uv[t] = acc[i][j + 1][q * 4 + t];
+  for (int i = 0; i < FM; ++i)
+    epilogue_row<GATEUP, FN>(e, g, m0 + wm * WTM + i * 32 + frow, M, n0 + wn * WTN, N, fhalf, acc[i]);
+}
+
+// Tail tiles of a gemm_bf16_mfma launch with the same arguments: adds each
+// tile's parts in part order and applies the epilogue.  One 64-lane
+// workgroup per (tail tile, wave, fragment row, column quad), grid-stride;
+// the parts are read 8 at a time so that many loads are in flight.
+template <class Cfg, bool GATEUP, class A, class E>
+__global__ void __launch_bounds__(64) gemm_bf16_fixup(A a, E e, int N, int K, int groups, int tiles_n, int P,
+                                                      const float* part) {
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, PB = 8;
+  const TailPlan plan = tail_plan(a, groups, tiles_n, K / Cfg::BK, P, true);
+  const int items = plan.tail * 8 * FM * 4;
+  const int lane = threadIdx.x, frow = lane & 31, fhalf = lane >> 5;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int ti = it / (8 * FM * 4), w = (it / (FM * 4)) % 8, i = (it / 4) % FM, q = it % 4;
+    const int wm = w >> 2, wn = w & 3, tid = w * 64 + lane;
+    int g, tm, tn;
+    tile_coords(a, groups, tiles_n, plan.total - plan.tail + ti, g, tm, tn);
+    const int m = tm * Cfg::BM + wm * Cfg::WTM + i * 32 + frow;
+    if (m >= a.rows(g)) continue;
+    const float4* src = (const float4*)(part + (int64_t)ti * plan.parts * PART_FLOATS);
+    float4 sum[FN];
+    for (int p0 = 0; p0 < plan.parts; p0 += PB) {
+      float4 x[PB][FN];
+#pragma unroll
+      for (int u = 0; u < PB; ++u)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (p0 + u < plan.parts) x[u][j] = src[(int64_t)(p0 + u) * (PART_FLOATS / 4) + ((i * FN + j) * 4 + q) * 512 + tid];
+#pragma unroll
+      for (int u = 0; u < PB; ++u)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (p0 + u < plan.parts) {
+            if (p0 + u == 0) {
+              sum[j] = x[u][j];
+            } else {
+              sum[j].x += x[u][j].x; sum[j].y += x[u][j].y; sum[j].z += x[u][j].z; sum[j].w += x[u][j].w;
             }
-            e.store4_pair(rc, (n >> 6) * 32 + (n & 31), gv, uv);
           }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WTN + j * 32 + q * 8 + fhalf * 4;
-          if (n < N) {
-            float v[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = acc[i][j][q * 4 + t];
-            e.store4(rc, n, N, v);
-          }
-        }
-      }
     }
+    float v[FN][4];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      v[j][0] = sum[j].x; v[j][1] = sum[j].y; v[j][2] = sum[j].z; v[j][3] = sum[j].w;
+    }
+    epilogue_q<GATEUP, FN>(e, e.row(g, m), tn * Cfg::BN + wn * Cfg::WTN, N, fhalf, q, v);
   }
 }
 

@@ -24,8 +24,10 @@
  *     and is asynchronous, except moe_capacity / moe_workspace_size (host
  *     only) and moe_drop_stats (synchronises `stream`).
  *   - `ws` is a caller-allocated device workspace of moe_workspace_size()
- *     bytes.  It carries counters and scan partials between the calls of one
- *     layer on one stream; calls that share a workspace must not overlap.
+ *     bytes.  It carries counters, scan partials and GEMM partial tiles
+ *     between the calls of one layer on one stream; calls that share a
+ *     workspace must not overlap, except moe_shared_experts, which touches
+ *     only its own region and may run beside the routed calls.
  *   - Activations and weights are bf16 (act_dtype 0) or fp32 (act_dtype 1);
  *     accumulation is fp32; logits and routing weights are fp32.
  *   - Return 0 (MOE_OK) or a negative MOE_E* code; moe_last_error() returns a
@@ -205,7 +207,8 @@ const char* moe_last_error(void);
  * stream.  Enabling adds two event records per launch; results are unchanged.
  * Labels: route_gemm, select_topk, send_rank, send_scan, pack, recv_rank,
  * recv_scan, recv_place, wave_gather, expert_gate_up, expert_down,
- * zero_dropped, combine, shared_gate_up, up_shared_down. */
+ * zero_dropped, combine, shared_gate_up, up_shared_down, and the tail-split
+ * fixups route_fixup, gate_up_fixup, down_fixup, up_fixup. */
 typedef struct moe_kernel_time {
   char name[32];    /* kernel label */
   int32_t launches; /* launches recorded since the last moe_timing_read */

@@ -63,7 +63,7 @@ def _check_routing(sh, ref_d, gl, gidx, gw, grid, what):
     np.testing.assert_allclose(gw, ref_d["w"], atol=1e-5, rtol=0, err_msg=f"{what}: topk_w")
 
 
-ALL = ["cfg1", "mini_bf16", "mini_bf16_skew", "mini_bf16_seg", "mini_f32"]
+ALL = ["cfg1", "mini_bf16", "mini_bf16_skew", "mini_bf16_seg", "mini_bf16_longk", "mini_f32"]
 
 
 @pytest.mark.parametrize("gather", ["fused", "buffer"])

@@ -105,6 +105,13 @@ MINI = {
                            shared_hidden=64, act="bf16",
                            emulate_all_ranks=True, bias="segments",
                            segment_tokens=100, segment_hot=4),
+    # long K (2048 and more) over few output tiles: every bf16 GEMM but the
+    # shared experts' gate/up takes the tail split along K
+    "mini_bf16_longk": Shape("mini_bf16_longk", tokens=300, d_model=2048,
+                             latent=2048, n_experts=24, top_k=2, n_ranks=4,
+                             waves=3, expert_hidden=1792, shared_experts=1,
+                             shared_hidden=512, act="bf16",
+                             emulate_all_ranks=True),
     # fp32 with ragged sizes everywhere
     "mini_f32": Shape("mini_f32", tokens=77, d_model=40, latent=24,
                       n_experts=12, top_k=3, n_ranks=3, waves=2,
