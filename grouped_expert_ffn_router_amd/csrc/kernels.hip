@@ -223,7 +223,7 @@ hipError_t launch_send_scan(const int32_t* chunk_count, int nch, int R, int cap,
 // One block per token: work out the k slots, then copy the latent row once
 // from HBM into every kept destination row (16 bytes per lane, coalesced).
 // Blocks past T mark the empty slots of every pool with id -1.
-constexpr int PACK_TPB = 128;
+constexpr int PACK_TPB = 384;  // one 16-byte chunk per lane of a 6 KB bf16 latent row
 
 __global__ void __launch_bounds__(PACK_TPB)
 pack_kernel(const char* __restrict__ z, int64_t row_bytes, const int32_t* __restrict__ idx,
@@ -456,7 +456,7 @@ template <> struct Vec8<float> {
   }
 };
 
-constexpr int COMBINE_TPB = 128;
+constexpr int COMBINE_TPB = 384;  // one 8-element chunk per lane of a 3072-wide latent row
 
 // One block per token: c = act(sum_i w_i * returned row i), i ascending, fp32.
 template <class T>
@@ -478,14 +478,23 @@ combine_kernel(const char* __restrict__ ret, int64_t dst_stride, int64_t row_byt
     ww[threadIdx.x] = w[(int64_t)t * k + threadIdx.x];
   }
   __syncthreads();
+  // The rows are read 8 at a time with every load issued before the sums
+  // (a missing row reads the first pool row and is then left out), so each
+  // lane keeps 8 loads in flight; the sum order stays i ascending.
   for (int c = threadIdx.x; c < L / 8; c += COMBINE_TPB) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < k; ++i) {
-      if (off[i] < 0) continue;
-      float f[8];
-      Vec8<T>::load((const T*)(ret + off[i]) + c * 8, f);
+    for (int i0 = 0; i0 < k; i0 += 8) {
+      float f[8][8];
+      bool use[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = fmaf(ww[i], f[q], acc[q]);
+      for (int u = 0; u < 8; ++u) {
+        use[u] = i0 + u < k && off[i0 + u] >= 0;
+        Vec8<T>::load((const T*)(ret + (use[u] ? off[i0 + u] : 0)) + c * 8, f[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = use[u] ? fmaf(ww[i0 + u], f[u][q], acc[q]) : acc[q];
     }
     Vec8<T>::store(c_out + (int64_t)t * ldc + c * 8, acc);
   }
