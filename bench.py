@@ -2,9 +2,11 @@
 
 One step = the whole layer for one batch of the rank's tokens: route (router
 + latent down-projection GEMM, top-k select) -> pack into the 64 fixed send
-pools -> (self-block of the dispatch exchange) -> 3 waves of receive + expert
-SwiGLU GEMMs (rows scattered into the return pools) -> (self-block of the
-return exchange) -> weighted combine + up-projection + shared experts.  The
+pools -> (self-block of the dispatch exchange) -> receive ranking -> 3 waves of
+placement + expert SwiGLU GEMMs (rows scattered into the return pools; odd
+waves on a second stream) -> (self-block of the return exchange) -> weighted
+combine + up-projection + shared experts (their gate/up GEMM on the second
+stream).  The
 pools the other 63 ranks send, and the rows they return, are seeded inputs
 resident in HBM before timing starts.  The metric is routed
 token-assignments per second: T * k / step time.
@@ -52,7 +54,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--gather", choices=["fused", "buffer"], default="fused")
     ap.add_argument("--streams", type=int, choices=[1, 2], default=2,
-                    help="2: the shared experts run on a second stream, beside the routed path")
+                    help="2: the shared experts and the odd waves run on a second stream, beside the routed "
+                         "path and the even waves")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens per rank of the CPU-oracle sample (0: the whole workload)")

@@ -167,6 +167,7 @@ int derive(const moe_dims* d, Q* q) {
 
 struct WsLayout {
   size_t ctr, s_cc, s_cb, s_lr, r_cc, r_cb, r_j, r_lr, r_rank, logits, h, cat, part, total;
+  size_t h_wave, part_wave;
   int nch_s, nch_r;
 };
 
@@ -190,9 +191,11 @@ WsLayout layout(const Q& q) {
   w.r_lr = take((size_t)q.R * q.scap * 4);
   w.r_rank = take((size_t)q.R * q.scap * 4);
   w.logits = take((size_t)q.T * q.E * 4);
-  w.h = take((size_t)q.WX * q.rcap * q.H * q.esize);
+  w.h_wave = (size_t)q.WX * q.rcap * q.H * q.esize;
+  w.h = take(w.h_wave * q.W);  // one SwiGLU hidden block per wave: waves may overlap
   w.cat = take((size_t)q.T * (q.L + q.S * q.HS) * q.esize);
-  w.part = take(q.bf16 ? (size_t)PART_SLOTS * PART_FLOATS * sizeof(float) : 0);  // tail-split partial tiles
+  w.part_wave = q.bf16 ? (size_t)PART_SLOTS * PART_FLOATS * sizeof(float) : 0;  // tail-split partial tiles
+  w.part = take(w.part_wave * (q.W + 1));  // one block per wave, one for route / combine
   w.total = off;
   return w;
 }
@@ -465,31 +468,49 @@ int moe_pack_pools(const moe_dims* dims, const void* z, const int32_t* topk_idx,
   return MOE_OK;
 }
 
-int moe_recv_waves(const moe_dims* dims, const void* recv_pools, int64_t src_stride_bytes, int32_t wave,
-                   void* wave_buf, int32_t* row_src, int32_t* wave_count, void* ws, void* stream) {
+int moe_recv_rank(const moe_dims* dims, const void* recv_pools, int64_t src_stride_bytes, void* ws, void* stream) {
   Q q;
   int rc = derive(dims, &q);
   if (rc) return rc;
-  NEED_IF(q.scap > 0, recv_pools, "recv_pools"); NEED4_IF(q.rcap > 0, row_src, "row_src");
-  NEED4(wave_count, "wave_count"); NEED(ws, "ws");
-  if (wave_buf && !aligned16(wave_buf)) return fail(MOE_EALIGN, "wave_buf is not 16-byte aligned");
-  if (wave < 0 || wave >= q.W) return fail(MOE_EINVAL, "wave %d out of range [0, %d)", wave, (int)q.W);
+  NEED_IF(q.scap > 0, recv_pools, "recv_pools"); NEED(ws, "ws");
   if (src_stride_bytes % 16 || src_stride_bytes < q.scap * q.prow)
     return fail(MOE_EALIGN, "src_stride_bytes must be a multiple of 16 and >= send_cap * pool_stride_bytes");
   const WsLayout w = layout(q);
   hipStream_t st = (hipStream_t)stream;
   int32_t* ctr = at<int32_t>(ws, w.ctr);
-  const int j0 = wave * (int)q.WX, nj = (int)q.WX, n_rows = (int)(q.R * q.scap);
+  const int n_rows = (int)(q.R * q.scap);
   int32_t* arrivals = ctr + Ctr::HEADER + 2 * q.R;
   int32_t* kept = arrivals + q.X;
   LAUNCH("recv_rank", st, launch_recv_rank(recv_pools, src_stride_bytes, q.prow, q.row_bytes, (int)q.R, (int)q.scap, (int)q.X,
                            (int)q.my_rank, at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cc),
-                           st), "moe_recv_waves rank");
-  LAUNCH("recv_scan", st, launch_recv_scan(at<int32_t>(ws, w.r_cc), w.nch_r, (int)q.X, (int)q.rcap, j0, nj, at<int32_t>(ws, w.r_cb),
-                           arrivals, kept, ctr + Ctr::RECV_BAD, wave_count, st), "moe_recv_waves scan");
-  LAUNCH("recv_place", st, launch_recv_place(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cb), n_rows,
-                            (int)q.X, (int)q.rcap, j0, nj, wave_count, at<int32_t>(ws, w.r_rank), row_src, st),
-          "moe_recv_waves place");
+                           st), "moe_recv_rank rank");
+  LAUNCH("recv_scan", st, launch_recv_scan(at<int32_t>(ws, w.r_cc), w.nch_r, (int)q.X, (int)q.rcap, at<int32_t>(ws, w.r_cb),
+                           arrivals, kept, ctr + Ctr::RECV_BAD, st), "moe_recv_rank scan");
+  LAUNCH("recv_final", st, launch_recv_final(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cb), n_rows,
+                            (int)q.X, at<int32_t>(ws, w.r_rank), st), "moe_recv_rank final");
+  return MOE_OK;
+}
+
+int moe_recv_waves(const moe_dims* dims, const void* recv_pools, int64_t src_stride_bytes, int32_t wave,
+                   void* wave_buf, int32_t* row_src, int32_t* wave_count, void* ws, void* stream) {
+  Q q;
+  int rc = derive(dims, &q);
+  if (rc) return rc;
+  NEED4_IF(q.rcap > 0, row_src, "row_src"); NEED4(wave_count, "wave_count"); NEED(ws, "ws");
+  if (wave_buf) {
+    if (!aligned16(wave_buf)) return fail(MOE_EALIGN, "wave_buf is not 16-byte aligned");
+    NEED_IF(q.scap > 0, recv_pools, "recv_pools (wave_buf is set)");
+    if (src_stride_bytes % 16 || src_stride_bytes < q.scap * q.prow)
+      return fail(MOE_EALIGN, "src_stride_bytes must be a multiple of 16 and >= send_cap * pool_stride_bytes");
+  }
+  if (wave < 0 || wave >= q.W) return fail(MOE_EINVAL, "wave %d out of range [0, %d)", wave, (int)q.W);
+  const WsLayout w = layout(q);
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* ctr = at<int32_t>(ws, w.ctr);
+  const int j0 = wave * (int)q.WX, nj = (int)q.WX, n_rows = (int)(q.R * q.scap);
+  const int32_t* kept = ctr + Ctr::HEADER + 2 * q.R + q.X;
+  LAUNCH("recv_place", st, launch_recv_place(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_rank), kept, n_rows, (int)q.rcap, j0,
+                            nj, wave_count, row_src, st), "moe_recv_waves place");
   if (wave_buf)
     LAUNCH("wave_gather", st, launch_wave_gather(recv_pools, src_stride_bytes, q.prow, (int)q.scap, q.row_bytes, row_src, wave_count,
                                nj, (int)q.rcap, wave_buf, st), "moe_recv_waves gather");
@@ -517,9 +538,10 @@ int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf, co
   const WsLayout w = layout(q);
   hipStream_t st = (hipStream_t)stream;
   hipError_t r;
-  float* part = at<float>(ws, w.part);
+  // the wave's own scratch (SwiGLU hidden rows, tail-split partials): waves may overlap
+  float* part = at<float>(ws, w.part + (size_t)(wave + 1) * w.part_wave);
   if (q.bf16) {
-    bf16_t* h = at<bf16_t>(ws, w.h);
+    bf16_t* h = at<bf16_t>(ws, w.h + (size_t)wave * w.h_wave);
     if (wave_buf) {
       ARows<bf16_t> a{(const bf16_t*)wave_buf, q.L, q.rcap * q.L, wave_count, 0};
       r = expert_gemms<bf16_t>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, part, st);
@@ -528,7 +550,7 @@ int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf, co
       r = expert_gemms<bf16_t>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, part, st);
     }
   } else {
-    float* h = at<float>(ws, w.h);
+    float* h = at<float>(ws, w.h + (size_t)wave * w.h_wave);
     if (wave_buf) {
       ARows<float> a{(const float*)wave_buf, q.L, q.rcap * q.L, wave_count, 0};
       r = expert_gemms<float>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, part, st);

@@ -314,63 +314,74 @@ hipError_t launch_recv_rank(const void* pools, int64_t src_stride, int64_t prow,
 }
 
 __global__ void __launch_bounds__(256)
-recv_scan_kernel(const int32_t* __restrict__ chunk_count, int nch, int X, int rcap, int j0, int nj,
-                 int32_t* __restrict__ chunk_base, int32_t* __restrict__ arrivals, int32_t* __restrict__ kept,
-                 int32_t* __restrict__ bad, int32_t* __restrict__ wave_count) {
+recv_scan_kernel(const int32_t* __restrict__ chunk_count, int nch, int X, int rcap, int32_t* __restrict__ chunk_base,
+                 int32_t* __restrict__ arrivals, int32_t* __restrict__ kept, int32_t* __restrict__ bad) {
   const int j = blockIdx.x;
   const int total = column_scan(chunk_count + (int64_t)j * nch, chunk_base + (int64_t)j * nch, nch);
   if (threadIdx.x == 0) {
     if (j < X) {
-      const int kp = min(total, rcap);
       arrivals[j] = total;
-      kept[j] = kp;
-      if (j >= j0 && j < j0 + nj) wave_count[j - j0] = kp;
+      kept[j] = min(total, rcap);
     } else {
       *bad = total;
     }
   }
 }
 
-hipError_t launch_recv_scan(const int32_t* chunk_count, int nch, int X, int rcap, int j0, int nj,
-                            int32_t* chunk_base, int32_t* arrivals, int32_t* kept, int32_t* bad,
-                            int32_t* wave_count, hipStream_t st) {
-  hipLaunchKernelGGL(recv_scan_kernel, dim3(X + 1), dim3(256), 0, st, chunk_count, nch, X, rcap, j0, nj,
-                     chunk_base, arrivals, kept, bad, wave_count);
+hipError_t launch_recv_scan(const int32_t* chunk_count, int nch, int X, int rcap, int32_t* chunk_base,
+                            int32_t* arrivals, int32_t* kept, int32_t* bad, hipStream_t st) {
+  hipLaunchKernelGGL(recv_scan_kernel, dim3(X + 1), dim3(256), 0, st, chunk_count, nch, X, rcap, chunk_base, arrivals,
+                     kept, bad);
   return hipGetLastError();
 }
 
-// Thread i: (a) final rank of receive row i, its row_src entry if it is kept
-// by an expert of this wave; (b) row_src slot i of the wave set to -1 if it
-// lies past that expert's count.
+// Final rank of every receive row within its local expert (-1: not one of
+// this rank's experts, or an empty slot).
 __global__ void __launch_bounds__(256)
-recv_place_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict__ row_lrank,
-                  const int32_t* __restrict__ chunk_base, int nch, int n_rows, int X, int rcap, int j0, int nj,
-                  const int32_t* __restrict__ wave_count, int32_t* __restrict__ row_rank,
-                  int32_t* __restrict__ row_src) {
+recv_final_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict__ row_lrank,
+                  const int32_t* __restrict__ chunk_base, int nch, int n_rows, int X,
+                  int32_t* __restrict__ row_rank) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_rows) return;
+  const int j = row_j[i];
+  row_rank[i] = (j >= 0 && j < X) ? chunk_base[(int64_t)j * nch + i / SCAN_CHUNK] + row_lrank[i] : -1;
+}
+
+hipError_t launch_recv_final(const int32_t* row_j, const int32_t* row_lrank, const int32_t* chunk_base, int n_rows,
+                             int X, int32_t* row_rank, hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  const int nch = (n_rows + SCAN_CHUNK - 1) / SCAN_CHUNK;
+  hipLaunchKernelGGL(recv_final_kernel, dim3((n_rows + 255) / 256), dim3(256), 0, st, row_j, row_lrank, chunk_base,
+                     nch, n_rows, X, row_rank);
+  return hipGetLastError();
+}
+
+// One wave: thread i (a) writes the row_src entry of receive row i if an
+// expert of the wave keeps it, (b) sets row_src slot i of the wave to -1 if it
+// lies past that expert's count; threads 0..nj-1 also write wave_count.
+// Reads only what moe_recv_rank left, so waves may run side by side.
+__global__ void __launch_bounds__(256)
+recv_place_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict__ row_rank,
+                  const int32_t* __restrict__ kept, int n_rows, int rcap, int j0, int nj,
+                  int32_t* __restrict__ wave_count, int32_t* __restrict__ row_src) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n_rows) {
-    const int j = row_j[i];
-    int rank = -1;
-    if (j >= 0 && j < X) {
-      rank = chunk_base[(int64_t)j * nch + i / SCAN_CHUNK] + row_lrank[i];
-      if (j >= j0 && j < j0 + nj && rank < rcap) row_src[(int64_t)(j - j0) * rcap + rank] = i;
-    }
-    row_rank[i] = rank;
+    const int j = row_j[i], rank = row_rank[i];
+    if (j >= j0 && j < j0 + nj && rank >= 0 && rank < rcap) row_src[(int64_t)(j - j0) * rcap + rank] = i;
   }
   if (i < nj * rcap) {
     const int jw = i / rcap, r = i - jw * rcap;
-    if (r >= wave_count[jw]) row_src[i] = -1;
+    if (r >= kept[j0 + jw]) row_src[i] = -1;
   }
+  if (i < nj) wave_count[i] = kept[j0 + i];
 }
 
-hipError_t launch_recv_place(const int32_t* row_j, const int32_t* row_lrank, const int32_t* chunk_base, int n_rows,
-                             int X, int rcap, int j0, int nj, const int32_t* wave_count, int32_t* row_rank,
-                             int32_t* row_src, hipStream_t st) {
-  const int nch = (n_rows + SCAN_CHUNK - 1) / SCAN_CHUNK;
-  const int n = max(n_rows, nj * rcap);
+hipError_t launch_recv_place(const int32_t* row_j, const int32_t* row_rank, const int32_t* kept, int n_rows,
+                             int rcap, int j0, int nj, int32_t* wave_count, int32_t* row_src, hipStream_t st) {
+  const int n = max(max(n_rows, nj * rcap), nj);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(recv_place_kernel, dim3((n + 255) / 256), dim3(256), 0, st, row_j, row_lrank, chunk_base, nch,
-                     n_rows, X, rcap, j0, nj, wave_count, row_rank, row_src);
+  hipLaunchKernelGGL(recv_place_kernel, dim3((n + 255) / 256), dim3(256), 0, st, row_j, row_rank, kept, n_rows, rcap,
+                     j0, nj, wave_count, row_src);
   return hipGetLastError();
 }
 

@@ -35,12 +35,12 @@ hipError_t launch_pack(const void* z, int64_t row_bytes, const int32_t* idx, con
 hipError_t launch_recv_rank(const void* pools, int64_t src_stride, int64_t pool_row_stride, int64_t id_off,
                             int R, int cap, int X, int my_rank, int32_t* row_j, int32_t* row_lrank,
                             int32_t* chunk_count, hipStream_t st);
-hipError_t launch_recv_scan(const int32_t* chunk_count, int nch, int X, int rcap, int j0, int nj,
-                            int32_t* chunk_base, int32_t* ctr_arrivals, int32_t* ctr_kept, int32_t* ctr_bad,
-                            int32_t* wave_count, hipStream_t st);
-hipError_t launch_recv_place(const int32_t* row_j, const int32_t* row_lrank, const int32_t* chunk_base,
-                             int n_rows, int X, int rcap, int j0, int nj, const int32_t* wave_count,
-                             int32_t* row_rank, int32_t* row_src, hipStream_t st);
+hipError_t launch_recv_scan(const int32_t* chunk_count, int nch, int X, int rcap, int32_t* chunk_base,
+                            int32_t* ctr_arrivals, int32_t* ctr_kept, int32_t* ctr_bad, hipStream_t st);
+hipError_t launch_recv_final(const int32_t* row_j, const int32_t* row_lrank, const int32_t* chunk_base, int n_rows,
+                             int X, int32_t* row_rank, hipStream_t st);
+hipError_t launch_recv_place(const int32_t* row_j, const int32_t* row_rank, const int32_t* ctr_kept, int n_rows,
+                             int rcap, int j0, int nj, int32_t* wave_count, int32_t* row_src, hipStream_t st);
 hipError_t launch_wave_gather(const void* pools, int64_t src_stride, int64_t pool_row_stride, int cap,
                               int64_t row_bytes, const int32_t* row_src, const int32_t* wave_count, int nj,
                               int rcap, void* wave_buf, hipStream_t st);

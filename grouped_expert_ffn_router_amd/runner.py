@@ -101,7 +101,7 @@ class OneRankLayer:
             self.ret_send = torch.zeros((R, self.scap, L), dtype=act, device=dev)
             self.ret_recv = upload(inp["foreign_ret"], dev)
             self.out = torch.empty((T, D), dtype=act, device=dev)
-            self._ev_go, self._ev_shared = torch.cuda.Event(), torch.cuda.Event()
+            self._ev_go, self._ev_shared, self._ev_ranked = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
         if "sources" in inp:
             self._route_other_ranks(inp["sources"])
 
@@ -139,6 +139,9 @@ class OneRankLayer:
         # self-block of the dispatch exchange
         self.recv_pools[self.rank].copy_(self.send_pools[self.rank])
 
+    def receive_rank(self, stream=None):
+        B.recv_rank(self.dims, self.recv_pools, self.scap * self.prow, self.ws, stream)
+
     def receive_wave(self, w, stream=None):
         B.recv_waves(self.dims, self.recv_pools, self.scap * self.prow, w, self.wave_buf, self.row_src[w],
                      self.wave_count[w], self.ws, stream)
@@ -159,27 +162,36 @@ class OneRankLayer:
 
     def run(self, stream=None, side=None):
         """One batch on `stream` (torch's current stream if None).  With `side`,
-        a second stream, the shared experts run there, concurrently with the
-        routed path: they start once everything queued before on `stream`
-        (the previous batch's combine, which reads their output) is done,
-        and the combine waits for them."""
+        a second stream, the shared experts and the odd waves run there,
+        beside the routed path and the even waves: the shared experts start
+        once everything queued before on `stream` (the previous batch's
+        combine, which reads their output) is done, the odd waves once the
+        receive ranking is, and the combine waits for both."""
         main = stream if stream is not None else torch.cuda.current_stream()
+        waves = self.shape.waves
         with torch.cuda.stream(main):
             if self.full:
                 if side is not None:
                     self._ev_go.record(main)
                     side.wait_event(self._ev_go)
                     self.shared(side)
-                    self._ev_shared.record(side)
                 else:
                     self.shared(main)
             self.dispatch(main)
-            for w in range(self.shape.waves):
-                self.receive_wave(w, main)
+            self.receive_rank(main)
+            # a shared wave buffer ("buffer" gather) keeps the waves in order
+            two = side is not None and self.full and self.wave_buf is None
+            if two:
+                self._ev_ranked.record(main)
+                side.wait_event(self._ev_ranked)
+            for w in range(waves):
+                st = side if two and w % 2 else main
+                self.receive_wave(w, st)
                 if self.full:
-                    self.expert_wave(w, main)
+                    self.expert_wave(w, st)
             if self.full:
                 if side is not None:
+                    self._ev_shared.record(side)
                     main.wait_event(self._ev_shared)
                 self.combine(main)
 
@@ -243,6 +255,7 @@ class AllRanksLayer:
         for r in range(R):
             d = self.dims[r]
             recv_view = self.pools[0, r]                 # pool from source s at + s * R * pool_bytes
+            B.recv_rank(d, recv_view, R * pool_bytes, self.ws[r], stream)
             for w in range(sh.waves):
                 B.recv_waves(d, recv_view, R * pool_bytes, w, self.wave_buf, self.row_src[r, w],
                              self.wave_count[r, w], self.ws[r], stream)

@@ -25,9 +25,10 @@
  *     only) and moe_drop_stats (synchronises `stream`).
  *   - `ws` is a caller-allocated device workspace of moe_workspace_size()
  *     bytes.  It carries counters, scan partials and GEMM partial tiles
- *     between the calls of one layer on one stream; calls that share a
- *     workspace must not overlap, except moe_shared_experts, which touches
- *     only its own region and may run beside the routed calls.
+ *     between the calls of one layer.  Calls that share a workspace run in
+ *     order on one stream, except: moe_shared_experts touches only its own
+ *     region and may run beside the routed calls, and after moe_recv_rank the
+ *     calls of different waves may run side by side.
  *   - Activations and weights are bf16 (act_dtype 0) or fp32 (act_dtype 1);
  *     accumulation is fp32; logits and routing weights are fp32.
  *   - Return 0 (MOE_OK) or a negative MOE_E* code; moe_last_error() returns a
@@ -132,14 +133,24 @@ int moe_pack_pools(const moe_dims* dims, const void* z, const int32_t* topk_idx,
                    void* send_pools, int64_t dst_stride_bytes, int32_t* slot_of,
                    int32_t* send_count, void* ws, void* stream);
 
-/* Receive side, one wave (section 二: receive capacity factor per local
- * expert; three waves of identical shape so that only part of the receive
- * bank is live at a time).  Wave w serves local experts w*X/W .. (w+1)*X/W-1.
- * Rows are visited source by source, slot by slot; a row with id e goes to
- * local expert e - X*my_rank, and the first recv_cap rows of each expert are
- * kept.
+/* Receive side, ranking (section 二: receive capacity factor per local
+ * expert).  Every row of every received pool is visited source by source,
+ * slot by slot; a row with id e goes to local expert e - X*my_rank, and the
+ * first recv_cap rows of each expert are kept.  The ranks, the per-expert
+ * arrival and kept counts and the count of rows with an id of no expert of
+ * this rank's domain stay in `ws` for moe_recv_waves, moe_expert_gemm and
+ * moe_drop_stats.  Once per layer, after the pools have arrived.
  *   recv_pools      pool from source s at recv_pools + s * src_stride_bytes
- *                   (send_cap rows of pool_stride_bytes, as moe_pack_pools)
+ *                   (send_cap rows of pool_stride_bytes, as moe_pack_pools) */
+int moe_recv_rank(const moe_dims* dims, const void* recv_pools, int64_t src_stride_bytes,
+                  void* ws, void* stream);
+
+/* Receive side, one wave (section 二: three waves of identical shape, so that
+ * only part of the receive bank is live at a time).  Wave w serves local
+ * experts w*X/W .. (w+1)*X/W-1 and reads only what moe_recv_rank left in
+ * `ws`: after it has completed, the calls of different waves (this one and
+ * moe_expert_gemm) may run side by side on different streams.
+ *   recv_pools      as for moe_recv_rank; read only when wave_buf is set
  *   wave_buf        NULL, or [X/W][recv_cap][L] act output: kept rows of the
  *                   wave's experts in rank order (rows past the count unwritten)
  *   row_src         [X/W][recv_cap] int32 output: s * send_cap + slot per kept
@@ -161,7 +172,9 @@ int moe_recv_waves(const moe_dims* dims, const void* recv_pools, int64_t src_str
  *   w13             [X][2H][L] act: per local expert, H gate rows then H up rows
  *   w2              [X][L][H] act
  *   ret_pools       return row of (s, slot) at ret_pools + s * ret_src_stride_bytes
- *                   + slot * L * sizeof(act) */
+ *                   + slot * L * sizeof(act)
+ * Each wave has its own scratch in `ws`, so waves may overlap (see
+ * moe_recv_waves); a wave_buf shared by two waves would not. */
 int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf,
                     const void* recv_pools, int64_t src_stride_bytes, const int32_t* row_src,
                     const int32_t* wave_count, const void* w13, const void* w2,
@@ -206,7 +219,7 @@ const char* moe_last_error(void);
  * on, so the elapsed time between them is that kernel's duration on its own
  * stream.  Enabling adds two event records per launch; results are unchanged.
  * Labels: route_gemm, select_topk, send_rank, send_scan, pack, recv_rank,
- * recv_scan, recv_place, wave_gather, expert_gate_up, expert_down,
+ * recv_scan, recv_final, recv_place, wave_gather, expert_gate_up, expert_down,
  * zero_dropped, combine, shared_gate_up, up_shared_down, and the tail-split
  * fixups route_fixup, gate_up_fixup, down_fixup, up_fixup. */
 typedef struct moe_kernel_time {

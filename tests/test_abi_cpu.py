@@ -82,5 +82,11 @@ def test_null_and_misaligned_pointers_are_rejected_before_any_launch():
         B.recv_waves(d, 256, 1127 * 6272, 3, None, 256, 256, 256, stream=0)
     assert e.value.code == B.MOE_EINVAL and "wave" in str(e.value)
     with pytest.raises(B.MoeError) as e:
+        B.recv_rank(d, None, 1127 * 6272, 256, stream=0)
+    assert e.value.code == B.MOE_EINVAL and "recv_pools" in str(e.value)
+    with pytest.raises(B.MoeError) as e:
+        B.recv_rank(d, 256, 1127 * 6272 + 8, 256, stream=0)
+    assert e.value.code == B.MOE_EALIGN
+    with pytest.raises(B.MoeError) as e:
         B.pack_pools(d, 256, 256, 256, 100, 256, 256, 256, stream=0)
     assert e.value.code == B.MOE_EALIGN
