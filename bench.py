@@ -20,6 +20,7 @@ Prints ONE JSON line with, besides the contract fields:
   cpu_baseline  the CPU oracle timed on a bounded sample of the same layer
 
 Options: --steps K --warmup W --config {2,3,4,5} --gather {fused,buffer} --streams {1,2}
+--sweep-capacity (one line per capacity-factor point instead of the benchmark line)
 --no-cpu-baseline --cpu-tokens N --seed S.  --gpus N > 1 exits: the benchmark
 measures one GPU.
 """
@@ -59,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens per rank of the CPU-oracle sample (0: the whole workload)")
+    ap.add_argument("--sweep-capacity", action="store_true",
+                    help="instead of the benchmark line: one JSON line per (send, receive) capacity factor "
+                         "with drop rates, exchange memory and throughput")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -145,12 +149,72 @@ def cpu_baseline(cfg, seed, tokens):
                       f"excluded, one run of {dt:.1f} s"}
 
 
+SWEEP_FACTORS = [(110, 115), (100, 115), (125, 115), (150, 115), (110, 100), (110, 130), (110, 150)]
+
+
+def capacity_sweep(args):
+    """Capacity factors vs drops, exchange memory and throughput (factors in percent).
+
+    The other ranks' tokens are drawn once and reused at every point; each
+    point rebuilds the layer (pools, returns and workspace sized by its
+    capacities) and times args.steps steps after args.warmup."""
+    from dataclasses import replace
+    import torch
+    from workload import configs, gen
+    from grouped_expert_ffn_router_amd import binding, runner
+    base = configs.get(args.config)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    drawn = None
+    for sn, rn in SWEEP_FACTORS:
+        sh = replace(base, send_num=sn, send_den=100, recv_num=rn, recv_den=100)
+        dims = binding.make_dims(sh)
+        scap, rcap, prow = binding.capacity(dims)
+        inp = gen.generate(sh, seed=args.seed, send_cap=scap)
+        if "sources" in inp:
+            if drawn is None:
+                drawn = {s: inp["sources"](s) for s in range(sh.n_ranks)}
+            inp["sources"] = drawn.__getitem__
+        lay = runner.OneRankLayer(sh, inp, device="cuda:0", gather=args.gather)
+        del inp
+        full = sh.layer == "full"
+        side = torch.cuda.Stream() if args.streams == 2 and full else None
+        for _ in range(args.warmup):
+            lay.run(stream, side)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            lay.run(stream, side)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        rep = lay.drop_report(stream)
+        es = 2 if sh.act == "bf16" else 4
+        pools = 2 * sh.n_ranks * scap * prow                          # send + receive pools
+        rets = 2 * sh.n_ranks * scap * sh.latent * es if full else 0   # returned rows, both ways
+        n_assign = sh.tokens * sh.top_k
+        print(json.dumps({
+            "sweep": "capacity", "workload": base.name, "send_factor": sn / 100, "recv_factor": rn / 100,
+            "send_cap": scap, "recv_cap": rcap,
+            "send_drop_rate": rep["send_dropped"] / n_assign,
+            "recv_drop_rate": rep["recv_dropped"] / max(sum(rep["expert_arrivals"]), 1),
+            "send_dropped": rep["send_dropped"], "recv_dropped": rep["recv_dropped"],
+            "exchange_bytes": pools + rets, "workspace_bytes": binding.workspace_size(dims),
+            "ms_per_step": ms, "assignments_per_s": n_assign / (ms * 1e-3)}), flush=True)
+        del lay
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU: one EP rank's share of the layer at its real "
                                    "shape; multi-GPU runs are not part of it", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.sweep_capacity:
+        capacity_sweep(args)
+        return
     import torch
     from workload import configs, gen
     from grouped_expert_ffn_router_amd import binding, runner

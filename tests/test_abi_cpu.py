@@ -46,6 +46,17 @@ def test_capacity_exact_integer_rounding():
         assert rcap == O.recv_capacity(T, sh.top_k, sh.n_ranks, sh.n_experts)
 
 
+@pytest.mark.parametrize("sn,sd,rn,rd", [(1, 1, 1, 1), (125, 100, 130, 100), (3, 2, 2, 1), (101, 100, 999, 1000)])
+def test_capacity_factors_as_rationals(sn, sd, rn, rd):
+    """The capacity factors are runtime rationals: the library and the oracle agree on the
+    rounded-up capacities for any of them (the capacity-factor sweep relies on this)."""
+    from dataclasses import replace
+    for cfg in (3, 5, "mini_bf16_skew"):
+        sh = replace(configs.get(cfg), send_num=sn, send_den=sd, recv_num=rn, recv_den=rd)
+        scap, rcap, _ = B.capacity(B.make_dims(sh))
+        assert (scap, rcap) == O.capacities(sh)
+
+
 def _bad(**kw):
     d = B.make_dims(configs.get(3))
     for k, v in kw.items():

@@ -131,6 +131,23 @@ def _check_all_ranks(sh, inp, ref, lay, grid):
         assert_bar(host(lay.out[s]), ref["out"][s]["out_exact"], act, f"src {s} out")
 
 
+@pytest.mark.parametrize("factors", [(1, 1, 1, 1), (125, 100, 100, 100), (100, 100, 150, 100), (2, 1, 2, 1)])
+@pytest.mark.parametrize("name", ["cfg1", "mini_bf16_skew"])
+def test_all_ranks_capacity_factors(runner, name, factors):
+    """Other send / receive capacity factors (the capacity-factor sweep): the same exact
+    routing, slots, ranks and drop counts as the oracle, floats within the bar."""
+    from dataclasses import replace
+    sn, sd, rn, rd = factors
+    sh = replace(_shape(name), send_num=sn, send_den=sd, recv_num=rn, recv_den=rd)
+    _say(f"[capacity] {name} send {sn}/{sd} recv {rn}/{rd}")
+    inp = gen.generate(sh, seed=5, grid=True)
+    ref = O.layer_all_ranks(sh, inp)
+    lay = runner.AllRanksLayer(sh, inp)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, True)
+
+
 @pytest.mark.parametrize("tokens", [0, 1, 65])
 def test_all_ranks_ragged_and_empty(runner, tokens):
     sh = configs.with_tokens(configs.get("mini_bf16"), tokens)

@@ -72,6 +72,21 @@ def test_capacities_against_the_pages_constants():
     assert O.recv_capacity(256, 2, 4, 24) == 99
 
 
+def test_capacities_at_other_factors():
+    # the factor multiplies the balanced load and the product is rounded up:
+    # closed forms at the 4K shape (T*k/R = 1024 rows per pool, R*T*k/E = 10922.67 per expert)
+    T, k, R, E = 8192, 8, 64, 384
+    assert O.send_capacity(T, k, R, 1, 1) == 1024
+    assert O.send_capacity(T, k, R, 125, 100) == 1280
+    assert O.send_capacity(T, k, R, 3, 2) == 1536
+    assert O.recv_capacity(T, k, R, E, 1, 1) == 10923          # ceil(32768 / 3)
+    assert O.recv_capacity(T, k, R, E, 130, 100) == 14200      # ceil(1.3 * 32768 / 3) = ceil(14199.47)
+    assert O.recv_capacity(T, k, R, E, 2, 1) == 21846          # ceil(65536 / 3)
+    for num, den in [(1, 1), (11, 10), (7, 5), (999, 1000)]:
+        for n in (1, 3, 50, 4097):
+            assert O.send_capacity(n, 1, 1, num, den) == math.ceil(Fraction(num, den) * n)
+
+
 def test_capacity_is_exact_where_float_ceil_is_not():
     # 1.10 * 50 is 55.000000000000007 in binary floating point
     assert math.ceil(1.10 * 50) == 56
