@@ -19,7 +19,7 @@ Prints ONE JSON line with, besides the contract fields:
   kernels       every kernel's average duration and roofline fraction
   cpu_baseline  the CPU oracle timed on a bounded sample of the same layer
 
-Options: --steps K --warmup W --config {2,3,4,5} --gather {fused,buffer} --streams {1,2}
+Options: --steps K --warmup W --config {2,3,4,5,6} --gather {fused,buffer} --streams {1,2}
 --sweep-capacity (one line per capacity-factor point instead of the benchmark line)
 --no-cpu-baseline --cpu-tokens N --seed S.  --gpus N > 1 exits: the benchmark
 measures one GPU.

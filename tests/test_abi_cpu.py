@@ -27,7 +27,7 @@ def test_library_exports_every_declared_entry_point():
         assert hasattr(lib, n), n
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, "mini_bf16", "mini_bf16_skew", "mini_bf16_seg", "mini_f32"])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, "mini_bf16", "mini_bf16_skew", "mini_bf16_seg", "mini_f32"])
 def test_capacity_matches_oracle(cfg):
     sh = configs.get(cfg)
     scap, rcap, stride = B.capacity(B.make_dims(sh))

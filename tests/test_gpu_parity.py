@@ -233,7 +233,7 @@ def _oracle_token_out(sh, inp, ref, tokens):
     return z, exact
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
 def test_one_rank_full_size(runner, cfg):
     sh = configs.get(cfg)
     scap, rcap = O.capacities(sh)

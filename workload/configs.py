@@ -63,7 +63,7 @@ class Shape:
 # one-rank layer at 4K context (8192 tokens = 2 sequences of 4096).  4: the
 # dispatch shape with a Zipf(1.1) per-expert router bias scaled to std 2.
 # 5: one 65536-token sequence per rank with routing correlated inside
-# 512-token segments.  In 2-4 the other 63 ranks' tokens go through the same
+# 512-token segments.  6: config 3 with the wider experts (hidden 3072).  In 2-4 the other 63 ranks' tokens go through the same
 # router; in 5 (64 x 65536 tokens would be 52 GB) their pools are drawn.
 CONFIGS = {
     1: Shape("cfg1_tiny_f32", tokens=256, d_model=64, latent=32, n_experts=24,
@@ -83,6 +83,11 @@ CONFIGS = {
              n_experts=384, top_k=8, n_ranks=64, waves=3, expert_hidden=1536,
              shared_experts=2, shared_hidden=1536, act="bf16", bias="segments",
              foreign="drawn"),
+    # the expert width the pages' parameter counts imply (routed and shared
+    # hidden 3072; about a third of the expert compute in the shared experts)
+    6: Shape("cfg6_full_layer_4k_h3072", tokens=8192, d_model=6144, latent=3072,
+             n_experts=384, top_k=8, n_ranks=64, waves=3, expert_hidden=3072,
+             shared_experts=2, shared_hidden=3072, act="bf16"),
 }
 
 # Small bf16 workloads for element-by-element parity: several GEMM tiles in
