@@ -20,7 +20,8 @@ Prints ONE JSON line with, besides the contract fields:
   cpu_baseline  the CPU oracle timed on a bounded sample of the same layer
 
 Options: --steps K --warmup W --config {2,3,4,5,6} --gather {fused,buffer} --streams {1,2}
---sweep-capacity (one line per capacity-factor point instead of the benchmark line)
+--sweep-capacity (one line per capacity-factor point instead of the benchmark line),
+--dropless (capacities fitted to the exchanged counts against the fixed factors)
 --no-cpu-baseline --cpu-tokens N --seed S.  --gpus N > 1 exits: the benchmark
 measures one GPU.
 """
@@ -63,6 +64,9 @@ def parse():
     ap.add_argument("--sweep-capacity", action="store_true",
                     help="instead of the benchmark line: one JSON line per (send, receive) capacity factor "
                          "with drop rates, exchange memory and throughput")
+    ap.add_argument("--dropless", action="store_true",
+                    help="instead of the benchmark line: the layer with capacities fitted exactly to the "
+                         "exchanged counts (no drops) against the fixed factors, one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -206,6 +210,79 @@ def capacity_sweep(args):
         torch.cuda.empty_cache()
 
 
+def dropless(args):
+    """Fixed capacity factors against capacities fitted exactly to the counts.
+
+    A dropless exchange first sends each destination its row count; with the
+    counts known, every pool can be sized to the largest demand and every
+    expert's bank to its largest arrivals, so nothing is dropped.  Three builds
+    of the one-rank layer (the other ranks' tokens drawn once): the fixed
+    factors (timed; its counts give the pool size), the exact send cap with a
+    receive cap no arrival can exceed (its arrivals give the bank size), and
+    both caps exact (timed, drop-free)."""
+    import torch
+    from workload import configs, gen
+    from grouped_expert_ffn_router_amd import binding, runner
+    base = configs.get(args.config)
+    if base.foreign != "routed":
+        raise SystemExit("--dropless needs a workload whose other ranks route their own tokens (configs 2, 3, 4, 6)")
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    drawn = {}
+
+    def build(sh):
+        scap, _, _ = binding.capacity(binding.make_dims(sh))
+        inp = gen.generate(sh, seed=args.seed, send_cap=scap)
+        if not drawn:
+            drawn.update({s: inp["sources"](s) for s in range(sh.n_ranks)})
+        inp["sources"] = drawn.__getitem__
+        return runner.OneRankLayer(sh, inp, device="cuda:0", gather=args.gather)
+
+    def measure(lay, timed):
+        side = torch.cuda.Stream() if args.streams == 2 and lay.full else None
+        for _ in range(args.warmup if timed else 1):
+            lay.run(stream, side)
+        torch.cuda.synchronize()
+        ms = None
+        if timed:
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(args.steps):
+                lay.run(stream, side)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / args.steps
+        return ms, lay.drop_report(stream)
+
+    def footprint(sh, lay):
+        es = 2 if sh.act == "bf16" else 4
+        rets = 2 * sh.n_ranks * lay.scap * sh.latent * es if lay.full else 0
+        return 2 * sh.n_ranks * lay.scap * lay.prow + rets + binding.workspace_size(lay.dims)
+
+    n_assign = base.tokens * base.top_k
+    lay = build(base)
+    ms_fixed, rep = measure(lay, True)
+    fixed = {"send_cap": lay.scap, "recv_cap": lay.rcap, "send_dropped": rep["send_dropped"],
+             "recv_dropped": rep["recv_dropped"], "bytes": footprint(base, lay), "ms_per_step": ms_fixed}
+    pool_rows = max(max(rep["send_demand"]), max(lay.source_demand.values(), default=0))
+    del lay
+    torch.cuda.empty_cache()
+    lay = build(configs.exact_fit(base, pool_rows, base.n_ranks * pool_rows))
+    _, rep = measure(lay, False)
+    expert_rows = max(rep["expert_arrivals"])
+    del lay
+    torch.cuda.empty_cache()
+    sh = configs.exact_fit(base, pool_rows, expert_rows)
+    lay = build(sh)
+    ms_fit, rep = measure(lay, True)
+    fit = {"send_cap": lay.scap, "recv_cap": lay.rcap, "send_dropped": rep["send_dropped"],
+           "recv_dropped": rep["recv_dropped"], "bytes": footprint(sh, lay), "ms_per_step": ms_fit}
+    print(json.dumps({"comparison": "dropless (capacities fitted to the exchanged counts) vs fixed factors",
+                      "workload": base.name, "fixed": fixed, "dropless": fit,
+                      "fixed_assignments_per_s": n_assign / (ms_fixed * 1e-3),
+                      "dropless_assignments_per_s": n_assign / (ms_fit * 1e-3)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -214,6 +291,9 @@ def main():
         sys.exit(2)
     if args.sweep_capacity:
         capacity_sweep(args)
+        return
+    if args.dropless:
+        dropless(args)
         return
     import torch
     from workload import configs, gen

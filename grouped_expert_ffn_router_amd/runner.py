@@ -102,6 +102,7 @@ class OneRankLayer:
             self.ret_recv = upload(inp["foreign_ret"], dev)
             self.out = torch.empty((T, D), dtype=act, device=dev)
             self._ev_go, self._ev_shared, self._ev_ranked = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
+        self.source_demand = {}
         if "sources" in inp:
             self._route_other_ranks(inp["sources"])
 
@@ -125,6 +126,9 @@ class OneRankLayer:
         B.pack_pools(d, self.z, self.idx, self.send_pools, self.scap * self.prow, self.slot_of, self.send_count,
                      self.ws)
         self.recv_pools[s].copy_(self.send_pools[self.rank])
+        # rows source s wants to send here, before its send cap (the count a
+        # dropless exchange would send ahead of the rows)
+        self.source_demand[s] = B.drop_stats(d, self.ws, raise_on_bad_ids=False).send_demand[self.rank]
 
     @property
     def esize(self):

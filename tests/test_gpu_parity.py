@@ -148,6 +148,33 @@ def test_all_ranks_capacity_factors(runner, name, factors):
     _check_all_ranks(sh, inp, ref, lay, True)
 
 
+@pytest.mark.parametrize("name", ["cfg1", "mini_bf16_skew"])
+def test_all_ranks_dropless_exact_fit(runner, name):
+    """Capacities fitted to the exchanged counts (the dropless comparison): the largest
+    demand of any pool and the largest arrivals at any expert, taken from the oracle
+    with caps nothing reaches.  Nothing drops, and the GPU layer matches the oracle,
+    which is then the textbook MoE layer."""
+    from dataclasses import replace
+    base = _shape(name)
+    inp = gen.generate(base, seed=6, grid=True)
+    n = base.tokens * base.top_k
+    wide = replace(base, send_num=base.n_ranks, send_den=1, recv_num=base.n_experts, recv_den=1)
+    ref0 = O.layer_all_ranks(wide, inp)
+    pool_rows = max(int(max(d["demand"])) for d in ref0["dispatch"])
+    expert_rows = max(int(max(rv["arrivals"])) for rv in ref0["recv"])
+    sh = configs.exact_fit(base, pool_rows, expert_rows)
+    assert O.capacities(sh) == (pool_rows, expert_rows)
+    _say(f"[dropless] {name} pool rows {pool_rows} expert rows {expert_rows}")
+    ref = O.layer_all_ranks(sh, inp)
+    assert ref["ledger"]["kept"] == base.n_ranks * n
+    lay = runner.AllRanksLayer(sh, inp)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, True)
+    reps = lay.drop_reports()
+    assert sum(r["send_dropped"] for r in reps) == 0 and sum(r["recv_dropped"] for r in reps) == 0
+
+
 @pytest.mark.parametrize("tokens", [0, 1, 65])
 def test_all_ranks_ragged_and_empty(runner, tokens):
     sh = configs.with_tokens(configs.get("mini_bf16"), tokens)

@@ -134,5 +134,18 @@ def get(cfg):
     return MINI[cfg]
 
 
+def exact_fit(shape, pool_rows, expert_rows):
+    """The shape with capacity factors that make the send cap exactly
+    ``pool_rows`` and the receive cap exactly ``expert_rows`` (the largest
+    demand of any pool and the largest arrivals at any expert, known once the
+    counts are exchanged): nothing is dropped, and every fixed buffer is as
+    small as that allows.  The factors stay exact rationals:
+    ceil(f * T*k/R) = pool_rows for f = pool_rows*R / (T*k), and likewise for
+    the receive cap over the balanced expert load R*T*k/E."""
+    n = shape.tokens * shape.top_k
+    return replace(shape, send_num=max(int(pool_rows), 1) * shape.n_ranks, send_den=max(n, 1),
+                   recv_num=max(int(expert_rows), 1) * shape.n_experts, recv_den=max(shape.n_ranks * n, 1))
+
+
 def with_tokens(shape, tokens):
     return replace(shape, tokens=tokens, name=f"{shape.name}_T{tokens}")
