@@ -219,7 +219,8 @@ def dropless(args):
     of the one-rank layer (the other ranks' tokens drawn once): the fixed
     factors (timed; its counts give the pool size), the exact send cap with a
     receive cap no arrival can exceed (its arrivals give the bank size), and
-    both caps exact (timed, drop-free)."""
+    both caps exact (timed, drop-free); then the ragged layout, whose pools
+    are laid end to end and hold exactly the rows sent (timed, drop-free)."""
     import torch
     from workload import configs, gen
     from grouped_expert_ffn_router_amd import binding, runner
@@ -230,13 +231,16 @@ def dropless(args):
     stream = torch.cuda.current_stream()
     drawn = {}
 
-    def build(sh):
+    def inputs(sh):
         scap, _, _ = binding.capacity(binding.make_dims(sh))
         inp = gen.generate(sh, seed=args.seed, send_cap=scap)
         if not drawn:
             drawn.update({s: inp["sources"](s) for s in range(sh.n_ranks)})
         inp["sources"] = drawn.__getitem__
-        return runner.OneRankLayer(sh, inp, device="cuda:0", gather=args.gather)
+        return inp
+
+    def build(sh):
+        return runner.OneRankLayer(sh, inputs(sh), device="cuda:0", gather=args.gather)
 
     def measure(lay, timed):
         side = torch.cuda.Stream() if args.streams == 2 and lay.full else None
@@ -277,10 +281,20 @@ def dropless(args):
     ms_fit, rep = measure(lay, True)
     fit = {"send_cap": lay.scap, "recv_cap": lay.rcap, "send_dropped": rep["send_dropped"],
            "recv_dropped": rep["recv_dropped"], "bytes": footprint(sh, lay), "ms_per_step": ms_fit}
-    print(json.dumps({"comparison": "dropless (capacities fitted to the exchanged counts) vs fixed factors",
-                      "workload": base.name, "fixed": fixed, "dropless": fit,
+    del lay
+    torch.cuda.empty_cache()
+    # ragged pools: laid end to end by destination, as long as the counts
+    lay = runner.RaggedOneRankLayer(base, inputs(sh), expert_rows, device="cuda:0", gather=args.gather)
+    ms_rag, rep = measure(lay, True)
+    rag = {"rows_sent": int(lay.own_off[-1]), "rows_received": lay.n_recv, "recv_cap": lay.rcap,
+           "send_dropped": rep["send_dropped"], "recv_dropped": rep["recv_dropped"], "bytes": lay.footprint(),
+           "ms_per_step": ms_rag}
+    print(json.dumps({"comparison": "dropless (capacities fitted to the exchanged counts; ragged pools) vs fixed "
+                                    "factors", "workload": base.name, "fixed": fixed, "dropless": fit,
+                      "ragged": rag,
                       "fixed_assignments_per_s": n_assign / (ms_fixed * 1e-3),
-                      "dropless_assignments_per_s": n_assign / (ms_fit * 1e-3)}), flush=True)
+                      "dropless_assignments_per_s": n_assign / (ms_fit * 1e-3),
+                      "ragged_assignments_per_s": n_assign / (ms_rag * 1e-3)}), flush=True)
 
 
 def main():

@@ -464,7 +464,30 @@ int moe_pack_pools(const moe_dims* dims, const void* z, const int32_t* topk_idx,
                            send_count, st), "moe_pack_pools scan");
   LAUNCH("pack", st, launch_pack(z, q.row_bytes, topk_idx, at<int32_t>(ws, w.s_lr), at<int32_t>(ws, w.s_cb), (int)q.T,
                       (int)q.k, (int)q.X, (int)q.E, (int)q.R, (int)q.scap, send_pools, dst_stride_bytes, q.prow,
-                      slot_of, send_count, st), "moe_pack_pools pack");
+                      slot_of, send_count, nullptr, st), "moe_pack_pools pack");
+  return MOE_OK;
+}
+
+int moe_pack_ragged(const moe_dims* dims, const void* z, const int32_t* topk_idx, void* send_rows,
+                    int32_t* send_off, int32_t* slot_of, int32_t* send_count, void* ws, void* stream) {
+  Q q;
+  int rc = derive(dims, &q);
+  if (rc) return rc;
+  NEED_IF(q.T > 0, send_rows, "send_rows"); NEED4(send_off, "send_off"); NEED4(send_count, "send_count");
+  NEED(ws, "ws");
+  if (q.T > 0) { NEED(z, "z"); NEED4(topk_idx, "topk_idx"); NEED4(slot_of, "slot_of"); }
+  const WsLayout w = layout(q);
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* ctr = at<int32_t>(ws, w.ctr);
+  const int no_cap = INT32_MAX;
+  LAUNCH("send_rank", st, launch_send_rank(topk_idx, (int)(q.T * q.k), (int)q.X, (int)q.E, (int)q.R, at<int32_t>(ws, w.s_lr),
+                           at<int32_t>(ws, w.s_cc), st), "moe_pack_ragged rank");
+  LAUNCH("send_scan", st, launch_send_scan(at<int32_t>(ws, w.s_cc), w.nch_s, (int)q.R, no_cap, at<int32_t>(ws, w.s_cb), ctr,
+                           send_count, st), "moe_pack_ragged scan");
+  LAUNCH("ragged_offsets", st, launch_ragged_offsets(send_count, (int)q.R, send_off, st), "moe_pack_ragged offsets");
+  LAUNCH("pack", st, launch_pack(z, q.row_bytes, topk_idx, at<int32_t>(ws, w.s_lr), at<int32_t>(ws, w.s_cb), (int)q.T,
+                      (int)q.k, (int)q.X, (int)q.E, (int)q.R, no_cap, send_rows, 0, q.prow, slot_of, send_count,
+                      send_off, st), "moe_pack_ragged pack");
   return MOE_OK;
 }
 

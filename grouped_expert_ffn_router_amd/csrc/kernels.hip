@@ -220,16 +220,32 @@ hipError_t launch_send_scan(const int32_t* chunk_count, int nch, int R, int cap,
   return hipGetLastError();
 }
 
+// Ragged layout: destination d's rows start at send_off[d], the exclusive
+// scan of the kept counts; send_off[R] is the total.
+__global__ void __launch_bounds__(256)
+ragged_offsets_kernel(const int32_t* __restrict__ send_count, int R, int32_t* __restrict__ send_off) {
+  const int total = column_scan(send_count, send_off, R);
+  if (threadIdx.x == 0) send_off[R] = total;
+}
+
+hipError_t launch_ragged_offsets(const int32_t* send_count, int R, int32_t* send_off, hipStream_t st) {
+  hipLaunchKernelGGL(ragged_offsets_kernel, dim3(1), dim3(256), 0, st, send_count, R, send_off);
+  return hipGetLastError();
+}
+
 // One block per token: work out the k slots, then copy the latent row once
 // from HBM into every kept destination row (16 bytes per lane, coalesced).
-// Blocks past T mark the empty slots of every pool with id -1.
+// Blocks past T mark the empty slots of every pool with id -1.  With
+// ragged_off set, the pools are laid end to end with no empty slots: the
+// r-th row kept for destination d is row ragged_off[d] + r.
 constexpr int PACK_TPB = 384;  // one 16-byte chunk per lane of a 6 KB bf16 latent row
 
 __global__ void __launch_bounds__(PACK_TPB)
 pack_kernel(const char* __restrict__ z, int64_t row_bytes, const int32_t* __restrict__ idx,
             const int32_t* __restrict__ local_rank, const int32_t* __restrict__ chunk_base, int nch, int T, int k,
             int X, int E, int R, int cap, char* __restrict__ pools, int64_t dst_stride, int64_t prow,
-            int32_t* __restrict__ slot_of, const int32_t* __restrict__ send_count) {
+            int32_t* __restrict__ slot_of, const int32_t* __restrict__ send_count,
+            const int32_t* __restrict__ ragged_off) {
   const int t = blockIdx.x;
   if (t >= T) {
     // empty-slot ids: slots [send_count[d], cap) of every pool d
@@ -250,7 +266,10 @@ pack_kernel(const char* __restrict__ z, int64_t row_bytes, const int32_t* __rest
     if (e >= 0 && e < E) {
       const int d = e / X;
       const int r = chunk_base[(int64_t)d * nch + (int)(a / SCAN_CHUNK)] + local_rank[a];
-      if (r < cap) {
+      if (ragged_off) {
+        slot = ragged_off[d] + r;
+        o = (int64_t)slot * prow;
+      } else if (r < cap) {
         slot = d * cap + r;
         o = d * dst_stride + (int64_t)r * prow;
       }
@@ -273,14 +292,15 @@ pack_kernel(const char* __restrict__ z, int64_t row_bytes, const int32_t* __rest
 
 hipError_t launch_pack(const void* z, int64_t row_bytes, const int32_t* idx, const int32_t* local_rank,
                        const int32_t* chunk_base, int T, int k, int X, int E, int R, int cap, void* pools,
-                       int64_t dst_stride, int64_t prow, int32_t* slot_of, const int32_t* send_count, hipStream_t st) {
+                       int64_t dst_stride, int64_t prow, int32_t* slot_of, const int32_t* send_count,
+                       const int32_t* ragged_off, hipStream_t st) {
   const int nch = (T * k + SCAN_CHUNK - 1) / SCAN_CHUNK;
-  const int64_t fill_blocks = ((int64_t)R * cap + PACK_TPB - 1) / PACK_TPB;
+  const int64_t fill_blocks = ragged_off ? 0 : ((int64_t)R * cap + PACK_TPB - 1) / PACK_TPB;
   const int64_t blocks = (int64_t)T + fill_blocks;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(PACK_TPB), 0, st, (const char*)z, row_bytes, idx,
                      local_rank, chunk_base, nch, T, k, X, E, R, cap, (char*)pools, dst_stride, prow, slot_of,
-                     send_count);
+                     send_count, ragged_off);
   return hipGetLastError();
 }
 

@@ -30,7 +30,8 @@ hipError_t launch_send_scan(const int32_t* chunk_count, int nch, int R, int cap,
 hipError_t launch_pack(const void* z, int64_t row_bytes, const int32_t* idx, const int32_t* local_rank,
                        const int32_t* chunk_base, int T, int k, int X, int E, int R, int cap, void* pools,
                        int64_t dst_stride, int64_t pool_row_stride, int32_t* slot_of, const int32_t* send_count,
-                       hipStream_t st);
+                       const int32_t* ragged_off, hipStream_t st);
+hipError_t launch_ragged_offsets(const int32_t* send_count, int R, int32_t* send_off, hipStream_t st);
 
 hipError_t launch_recv_rank(const void* pools, int64_t src_stride, int64_t pool_row_stride, int64_t id_off,
                             int R, int cap, int X, int my_rank, int32_t* row_j, int32_t* row_lrank,

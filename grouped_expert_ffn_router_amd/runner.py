@@ -203,6 +203,148 @@ class OneRankLayer:
         return B.drop_stats(self.dims, self.ws, stream, raise_on_bad_ids=False).as_dict()
 
 
+class RaggedOneRankLayer(OneRankLayer):
+    """One EP rank's layer with the dropless ragged exchange (the counterpart of
+    RaggedAllRanksLayer at one rank's real shape).  The rank packs its rows
+    back to back by destination (moe_pack_ragged, no send cap).  At set-up the
+    other ranks route and pack their own tokens the same way (untimed: it
+    stands for the other GPUs) and their counts toward this rank fix where
+    every source's segment sits in the receive buffer; the inputs are the same
+    every step, so the counts are too, and a step copies only the self
+    segments of the two exchanges.  ``foreign_ret`` rows (the rows the other
+    ranks return, [R][pool_rows][L]) are laid into this rank's ragged order
+    once.  ``expert_rows`` is the receive cap of every expert."""
+
+    def __init__(self, shape, inp, expert_rows, device="cuda", gather="fused"):
+        from workload.configs import exact_fit
+        if "sources" not in inp:
+            raise ValueError("the ragged layer needs a workload whose other ranks route their own tokens")
+        self.shape, self.device, self.gather = shape, device, gather
+        r = int(inp["receiver"])
+        self.rank = r
+        T, D, L, E, k, R = shape.tokens, shape.d_model, shape.latent, shape.n_experts, shape.top_k, shape.n_ranks
+        X, W = shape.local_experts, shape.waves
+        WX = X // W
+        act = _act(shape)
+        dev = device
+        self.full = shape.layer == "full"
+        self._fit = lambda pool_rows: exact_fit(shape, pool_rows, int(expert_rows))
+        # set-up dims: neither cap is used by route and pack, and cap 1 keeps
+        # the receive parts of the set-up workspace small
+        setup_dims = B.make_dims(exact_fit(shape, 1, 1), my_rank=r)
+        self.rcap = int(expert_rows)
+        self.prow = B.capacity(setup_dims)[2]
+        self.x = upload(inp["x"], dev)
+        self.w_router = upload(inp["w_router"], dev)
+        self.w_down = upload(inp["w_down"], dev)
+        self.bias = None if inp["bias"] is None else upload(np.ascontiguousarray(inp["bias"], np.float32), dev)
+        self.bias_row_tokens = int(inp["bias_row_tokens"])
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.z = torch.empty((T, L), dtype=act, device=dev)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.send_rows = torch.empty((T * k, self.prow), dtype=torch.uint8, device=dev)
+        self.send_off = torch.empty((R + 1,), dtype=torch.int32, device=dev)
+        self.slot_of = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.send_count = torch.empty((R,), dtype=torch.int32, device=dev)
+        ws_setup = torch.zeros((B.workspace_size(setup_dims),), dtype=torch.uint8, device=dev)
+        # the other ranks' segments toward this rank, and this rank's own count
+        segs = {}
+        for s in range(R):
+            host_x = inp["x"] if s == r else inp["sources"](s)
+            xs = upload(host_x, dev)
+            B.route(setup_dims, xs, self.w_router, self.w_down, self.bias, self.bias_row_tokens, self.logits,
+                    self.z, self.idx, self.w, ws_setup)
+            B.pack_ragged(setup_dims, self.z, self.idx, self.send_rows, self.send_off, self.slot_of,
+                          self.send_count, ws_setup)
+            off = self.send_off.cpu().numpy()
+            segs[s] = self.send_rows[int(off[r]):int(off[r + 1])].clone() if s != r else None
+            if s == r:
+                self.own_off = off.astype(np.int64)
+        cnt = np.array([segs[s].shape[0] if s != r else self.own_off[r + 1] - self.own_off[r] for s in range(R)],
+                       dtype=np.int64)
+        self.seg_off = np.concatenate([[0], np.cumsum(cnt)])
+        self.n_recv = int(self.seg_off[-1])
+        self.view_rows = max(-(-self.n_recv // R), 1)
+        self.recv_dims = B.make_dims(self._fit(self.view_rows), my_rank=r)
+        assert B.capacity(self.recv_dims)[:2] == (self.view_rows, self.rcap)
+        self.scap = self.view_rows
+        self.recv_pools = torch.empty((R * self.view_rows, self.prow), dtype=torch.uint8, device=dev)
+        self.recv_pools.view(torch.int32)[self.n_recv:, (L * self.esize) // 4] = -1
+        for s in range(R):
+            if s != r and cnt[s]:
+                self.recv_pools[self.seg_off[s]:self.seg_off[s + 1]].copy_(segs[s])
+        del segs, ws_setup
+        # one workspace and one set of dims for the whole step (moe_pack_ragged
+        # ignores the send cap, moe_combine reads the ragged return rows with
+        # any cap)
+        self.dims = self.recv_dims
+        self.ws = self.ws_recv = torch.zeros((B.workspace_size(self.recv_dims),), dtype=torch.uint8, device=dev)
+        self.row_src = torch.empty((W, WX, self.rcap), dtype=torch.int32, device=dev)
+        self.wave_count = torch.empty((W, WX), dtype=torch.int32, device=dev)
+        self.wave_buf = torch.empty((WX, self.rcap, L), dtype=act, device=dev) if gather == "buffer" else None
+        self.source_demand = {s: int(cnt[s]) for s in range(R) if s != r}
+        if self.full:
+            self.w13 = upload(inp["w13"], dev)
+            self.w2 = upload(inp["w2"], dev)
+            self.w_up = upload(inp["w_up"], dev)
+            self.ws13 = upload(inp["ws13"], dev)
+            self.ws2 = upload(inp["ws2"], dev)
+            self.ret_send = torch.zeros((R * self.view_rows, L), dtype=act, device=dev)
+            self.ret_back = torch.zeros((T * k, L), dtype=act, device=dev)
+            fr = upload(inp["foreign_ret"], dev)                 # [R][pool_rows][L]
+            own_cnt = np.diff(self.own_off)
+            for d in range(R):
+                c = int(own_cnt[d])
+                if d != r and c:
+                    assert c <= fr.shape[1], "foreign_ret has fewer rows than this rank sends"
+                    self.ret_back[self.own_off[d]:self.own_off[d] + c].copy_(fr[d, :c])
+            del fr
+            self.out = torch.empty((T, D), dtype=act, device=dev)
+            self._ev_go, self._ev_shared, self._ev_ranked = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
+        torch.cuda.synchronize()
+
+    def dispatch(self, stream=None):
+        d, r = self.dims, self.rank
+        B.route(d, self.x, self.w_router, self.w_down, self.bias, self.bias_row_tokens, self.logits, self.z,
+                self.idx, self.w, self.ws, stream)
+        B.pack_ragged(d, self.z, self.idx, self.send_rows, self.send_off, self.slot_of, self.send_count, self.ws,
+                      stream)
+        # self segment of the dispatch exchange (its place fixed by the count exchange)
+        c = int(self.own_off[r + 1] - self.own_off[r])
+        if c:
+            self.recv_pools[self.seg_off[r]:self.seg_off[r] + c].copy_(
+                self.send_rows[self.own_off[r]:self.own_off[r] + c])
+
+    def receive_rank(self, stream=None):
+        B.recv_rank(self.recv_dims, self.recv_pools, self.view_rows * self.prow, self.ws_recv, stream)
+
+    def receive_wave(self, w, stream=None):
+        B.recv_waves(self.recv_dims, self.recv_pools, self.view_rows * self.prow, w, self.wave_buf, self.row_src[w],
+                     self.wave_count[w], self.ws_recv, stream)
+
+    def expert_wave(self, w, stream=None):
+        B.expert_gemm(self.recv_dims, w, self.wave_buf, self.recv_pools, self.view_rows * self.prow,
+                      self.row_src[w], self.wave_count[w], self.w13, self.w2, self.ret_send,
+                      self.view_rows * self.shape.latent * self.esize, self.ws_recv, stream)
+
+    def combine(self, stream=None):
+        r = self.rank
+        c = int(self.own_off[r + 1] - self.own_off[r])
+        if c:   # self segment of the return exchange
+            self.ret_back[self.own_off[r]:self.own_off[r] + c].copy_(self.ret_send[self.seg_off[r]:self.seg_off[r] + c])
+        scap = B.capacity(self.dims)[0]
+        B.combine(self.dims, self.ret_back, scap * self.shape.latent * self.esize, self.slot_of, self.w, self.w_up,
+                  self.ws2, self.out, self.ws, stream)
+
+    def footprint(self):
+        """Bytes of the exchange buffers and the workspace."""
+        n = self.send_rows.numel() + self.recv_pools.numel() + self.ws.numel()
+        if self.full:
+            n += (self.ret_send.numel() + self.ret_back.numel()) * self.esize
+        return n
+
+
 class AllRanksLayer:
     """Every rank of a small EP domain on one device (zero-copy exchanges)."""
 
@@ -276,3 +418,131 @@ class AllRanksLayer:
     def drop_reports(self, stream=None):
         return [B.drop_stats(self.dims[r], self.ws[r], stream, raise_on_bad_ids=False).as_dict()
                 for r in range(self.shape.n_ranks)]
+
+
+def _ceil_div(a, b):
+    return -(-a // b)
+
+
+class RaggedAllRanksLayer:
+    """Every rank of a small EP domain on one device with the dropless ragged
+    exchange: each rank packs its rows back to back by destination
+    (moe_pack_ragged) and nothing is capped on the send side.  The row counts
+    are exchanged first (a host read of send_count here); each receiver's
+    buffer then holds the segments sent to it laid end to end, source by
+    source, viewed by the receive calls as R pools of ceil(n/R) rows with id
+    -1 past the n received rows; the return rows go back into each sender's
+    ragged order.  The two exchanges are device copies standing for the
+    ragged all-to-all.  ``expert_rows`` sizes every expert's bank (the
+    receive cap)."""
+
+    def __init__(self, shape, inp, expert_rows, device="cuda", gather="fused"):
+        from workload.configs import exact_fit
+        self.shape, self.device, self.gather = shape, device, gather
+        T, D, L, E, k, R = shape.tokens, shape.d_model, shape.latent, shape.n_experts, shape.top_k, shape.n_ranks
+        X, W = shape.local_experts, shape.waves
+        WX = X // W
+        act = _act(shape)
+        dev = device
+        self.expert_rows = int(expert_rows)
+        self._fit = lambda pool_rows: exact_fit(shape, pool_rows, self.expert_rows)
+        # send side (route, pack, shared experts, combine): neither cap is used,
+        # and cap 1 keeps the receive parts of its workspace small
+        self.send_dims = [B.make_dims(exact_fit(shape, 1, 1), my_rank=r) for r in range(R)]
+        self.rcap = self.expert_rows
+        self.prow = B.capacity(self.send_dims[0])[2]
+        self.x = upload(inp["x"], dev)
+        self.w_router = upload(inp["w_router"], dev)
+        self.w_down = upload(inp["w_down"], dev)
+        bias = inp["bias"]
+        if bias is not None and bias.ndim == 2:
+            bias = np.broadcast_to(bias, (R,) + bias.shape)
+        self.bias = None if bias is None else upload(np.ascontiguousarray(bias, np.float32), dev)
+        self.bias_row_tokens = int(inp["bias_row_tokens"])
+        self.w13 = upload(inp["w13"], dev)
+        self.w2 = upload(inp["w2"], dev)
+        self.w_up = upload(inp["w_up"], dev)
+        self.ws13 = upload(inp["ws13"], dev)
+        self.ws2 = upload(inp["ws2"], dev)
+        self.logits = torch.empty((R, T, E), dtype=torch.float32, device=dev)
+        self.z = torch.empty((R, T, L), dtype=act, device=dev)
+        self.idx = torch.empty((R, T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((R, T, k), dtype=torch.float32, device=dev)
+        self.send_rows = torch.empty((R, T * k, self.prow), dtype=torch.uint8, device=dev)
+        self.send_off = torch.empty((R, R + 1), dtype=torch.int32, device=dev)
+        self.slot_of = torch.empty((R, T, k), dtype=torch.int32, device=dev)
+        self.send_count = torch.empty((R, R), dtype=torch.int32, device=dev)
+        self.ret_back = torch.zeros((R, T * k, L), dtype=act, device=dev)   # returned rows, sender's order
+        self.row_src = torch.empty((R, W, WX, self.rcap), dtype=torch.int32, device=dev)
+        self.wave_count = torch.empty((R, W, WX), dtype=torch.int32, device=dev)
+        self.wave_buf = torch.empty((WX, self.rcap, L), dtype=act, device=dev) if gather == "buffer" else None
+        self.out = torch.empty((R, T, D), dtype=act, device=dev)
+        self.ws_send = [torch.zeros((B.workspace_size(d),), dtype=torch.uint8, device=dev) for d in self.send_dims]
+        self.recv_dims, self.recv, self.ret, self.ws_recv, self.seg_off = [], [], [], [], []
+
+    def run(self, stream=None):
+        sh = self.shape
+        R, L, X = sh.n_ranks, sh.latent, sh.local_experts
+        esize = 2 if sh.act == "bf16" else 4
+        for s in range(R):
+            d = self.send_dims[s]
+            bias = None if self.bias is None else self.bias[s]
+            B.route(d, self.x[s], self.w_router, self.w_down, bias, self.bias_row_tokens, self.logits[s],
+                    self.z[s], self.idx[s], self.w[s], self.ws_send[s], stream)
+            B.pack_ragged(d, self.z[s], self.idx[s], self.send_rows[s], self.send_off[s], self.slot_of[s],
+                          self.send_count[s], self.ws_send[s], stream)
+        # the count exchange
+        torch.cuda.synchronize()
+        cnt = self.send_count.cpu().numpy().astype(np.int64)      # [src][dst]
+        off = self.send_off.cpu().numpy().astype(np.int64)        # [src][R+1]
+        self.recv_dims, self.recv, self.ret, self.ws_recv, self.seg_off = [], [], [], [], []
+        id_col = (L * esize) // 4
+        for r in range(R):
+            n = int(cnt[:, r].sum())
+            view_rows = max(_ceil_div(n, R), 1)
+            d = B.make_dims(self._fit(view_rows), my_rank=r)
+            assert B.capacity(d)[:2] == (view_rows, self.rcap)
+            seg = np.concatenate([[0], np.cumsum(cnt[:, r])])
+            buf = torch.empty((R * view_rows, self.prow), dtype=torch.uint8, device=self.device)
+            buf.view(torch.int32)[n:, id_col] = -1
+            for s in range(R):                                  # the dispatch exchange
+                c = int(cnt[s, r])
+                if c:
+                    buf[seg[s]:seg[s] + c].copy_(self.send_rows[s, off[s, r]:off[s, r] + c])
+            ws = torch.zeros((B.workspace_size(d),), dtype=torch.uint8, device=self.device)
+            ret = torch.zeros((R * view_rows, L), dtype=self.out.dtype, device=self.device)
+            pool_bytes = view_rows * self.prow
+            B.recv_rank(d, buf, pool_bytes, ws, stream)
+            for w in range(sh.waves):
+                B.recv_waves(d, buf, pool_bytes, w, self.wave_buf, self.row_src[r, w], self.wave_count[r, w], ws,
+                             stream)
+                B.expert_gemm(d, w, self.wave_buf, buf, pool_bytes, self.row_src[r, w], self.wave_count[r, w],
+                              self.w13[r * X:(r + 1) * X], self.w2[r * X:(r + 1) * X], ret, view_rows * L * esize,
+                              ws, stream)
+            for s in range(R):                                  # the return exchange
+                c = int(cnt[s, r])
+                if c:
+                    self.ret_back[s, off[s, r]:off[s, r] + c].copy_(ret[seg[s]:seg[s] + c])
+            self.recv_dims.append(d)
+            self.recv.append(buf)
+            self.ret.append(ret)
+            self.ws_recv.append(ws)
+            self.seg_off.append(seg)
+        for s in range(R):
+            d = self.send_dims[s]
+            B.shared_experts(d, self.x[s], self.ws13, self.ws_send[s], stream)
+            scap = B.capacity(d)[0]
+            B.combine(d, self.ret_back[s], scap * L * esize, self.slot_of[s], self.w[s], self.w_up, self.ws2,
+                      self.out[s], self.ws_send[s], stream)
+
+    def drop_reports(self, stream=None):
+        """Send fields from each rank's dispatch, receive fields from its receive."""
+        out = []
+        for r in range(self.shape.n_ranks):
+            snd = B.drop_stats(self.send_dims[r], self.ws_send[r], stream, raise_on_bad_ids=False).as_dict()
+            rcv = B.drop_stats(self.recv_dims[r], self.ws_recv[r], stream, raise_on_bad_ids=False).as_dict()
+            for key in ("recv_arrivals", "recv_kept", "recv_dropped", "recv_bad_ids", "expert_arrivals",
+                        "expert_kept"):
+                snd[key] = rcv[key]
+            out.append(snd)
+        return out

@@ -133,6 +133,33 @@ int moe_pack_pools(const moe_dims* dims, const void* z, const int32_t* topk_idx,
                    void* send_pools, int64_t dst_stride_bytes, int32_t* slot_of,
                    int32_t* send_count, void* ws, void* stream);
 
+/* Ragged packing for the dropless comparison (section 四 of the same page:
+ * the first fallback is a dropless all-to-all whose row counts travel ahead
+ * of the rows, so pools can be ragged).  No send cap applies: every valid
+ * assignment is kept.  Assignment (t, i) goes to rank topk_idx[t][i] / X and
+ * is ranked in (t, i) order within its destination, as in moe_pack_pools;
+ * the pools are laid end to end, destination by destination, with no empty
+ * rows.  The send capacity factor in dims is not used.
+ *   send_rows   [T*k][pool_stride_bytes]: the r-th row for destination d is
+ *               row send_off[d] + r (L act values, then the int32 global
+ *               expert id); rows past send_off[R] are left unwritten
+ *   send_off    [R+1] int32 output: exclusive scan of send_count; send_off[R]
+ *               is the number of rows written
+ *   slot_of     [T][k] int32 output: send_off[d] + r (a row index), or -1 for
+ *               an invalid expert id
+ *   send_count  [R] int32 output: rows per destination (= its demand)
+ * The rest of the layer takes this layout as R pools of send_cap rows laid
+ * end to end: moe_combine with ret_dst_stride_bytes = send_cap * L *
+ * sizeof(act) reads return row s at s * L * sizeof(act) for any s, so the
+ * return rows can sit in this same ragged order (at least send_off[R] rows).
+ * On the receive side, a buffer of the received segments laid end to end is
+ * R pools of send_cap rows with src_stride_bytes = send_cap *
+ * pool_stride_bytes, once send_cap * R covers the received rows and the
+ * rows past them carry id -1. */
+int moe_pack_ragged(const moe_dims* dims, const void* z, const int32_t* topk_idx,
+                    void* send_rows, int32_t* send_off, int32_t* slot_of,
+                    int32_t* send_count, void* ws, void* stream);
+
 /* Receive side, ranking (section 二: receive capacity factor per local
  * expert).  Every row of every received pool is visited source by source,
  * slot by slot; a row with id e goes to local expert e - X*my_rank, and the

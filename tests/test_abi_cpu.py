@@ -101,3 +101,12 @@ def test_null_and_misaligned_pointers_are_rejected_before_any_launch():
     with pytest.raises(B.MoeError) as e:
         B.pack_pools(d, 256, 256, 256, 100, 256, 256, 256, stream=0)
     assert e.value.code == B.MOE_EALIGN
+    with pytest.raises(B.MoeError) as e:
+        B.pack_ragged(d, 256, 256, 256, None, 256, 256, 256, stream=0)
+    assert e.value.code == B.MOE_EINVAL and "send_off" in str(e.value)
+    with pytest.raises(B.MoeError) as e:
+        B.pack_ragged(d, 256, 256, None, 256, 256, 256, 256, stream=0)
+    assert e.value.code == B.MOE_EINVAL and "send_rows" in str(e.value)
+    with pytest.raises(B.MoeError) as e:
+        B.pack_ragged(d, 256, 256, 256, 258, 256, 256, 256, stream=0)
+    assert e.value.code == B.MOE_EALIGN

@@ -175,6 +175,87 @@ def test_all_ranks_dropless_exact_fit(runner, name):
     assert sum(r["send_dropped"] for r in reps) == 0 and sum(r["recv_dropped"] for r in reps) == 0
 
 
+def _dropless_caps(base, inp):
+    """(pool_rows, expert_rows): the largest demand of any pool and the largest
+    arrivals at any expert, from the oracle with caps nothing reaches."""
+    wide = replace(base, send_num=base.n_ranks, send_den=1, recv_num=base.n_experts, recv_den=1)
+    ref0 = O.layer_all_ranks(wide, inp)
+    return (max(int(max(d["demand"])) for d in ref0["dispatch"]),
+            max(int(max(rv["arrivals"])) for rv in ref0["recv"]))
+
+
+@pytest.mark.parametrize("gather", ["fused", "buffer"])
+@pytest.mark.parametrize("name", ["cfg1", "mini_bf16_skew", "mini_bf16"])
+def test_all_ranks_ragged_dropless(runner, name, gather):
+    """The ragged dropless exchange (pools laid end to end by destination, no send
+    cap, receive buffers as long as what arrives): every integer result is the
+    oracle's drop-free one moved to the ragged row order -- slot_of = offset of
+    the destination + rank, row_src = offset of the source segment + slot -- and
+    the floats match the oracle's textbook layer within the bar."""
+    base = _shape(name)
+    inp = gen.generate(base, seed=6, grid=True)
+    pool_rows, expert_rows = _dropless_caps(base, inp)
+    sh = configs.exact_fit(base, pool_rows, expert_rows)
+    _say(f"[ragged] {name} gather={gather} pool rows {pool_rows} expert rows {expert_rows}")
+    ref = O.layer_all_ranks(sh, inp)
+    assert ref["ledger"]["kept"] == base.n_ranks * base.tokens * base.top_k
+    lay = runner.RaggedAllRanksLayer(base, inp, expert_rows, gather=gather)
+    lay.run()
+    torch.cuda.synchronize()
+    R, L, act, k = base.n_ranks, base.latent, base.act, base.top_k
+    reps = lay.drop_reports()
+    tok = np.repeat(np.arange(base.tokens), k)
+    for s in range(R):
+        d = ref["dispatch"][s]
+        _check_routing(base, d, host(lay.logits[s]), host(lay.idx[s]), host(lay.w[s]), True, f"src {s}")
+        gz = host(lay.z[s])
+        assert np.array_equal(gz, d["z"]), f"src {s}: z differs on the grid"
+        cnt = host(lay.send_count[s])
+        assert np.array_equal(cnt, d["demand"]), f"src {s}: send_count"
+        off = host(lay.send_off[s])
+        assert off[0] == 0 and np.array_equal(np.diff(off), cnt), f"src {s}: send_off"
+        so = d["slot_of"].reshape(-1)
+        assert np.all(so >= 0)
+        dest, rank = so // pool_rows, so % pool_rows
+        want = off[dest] + rank
+        assert np.array_equal(host(lay.slot_of[s]).reshape(-1), want), f"src {s}: ragged slot_of"
+        ids, rows = _decode_pools(lay.send_rows[s, :off[R]], L, act)
+        assert np.array_equal(ids[want], d["idx"].reshape(-1)), f"src {s}: row ids"
+        assert np.array_equal(rows[want], gz[tok]), f"src {s}: row payload != z rows"
+        rp = reps[s]
+        assert rp["send_dropped"] == 0 and rp["send_kept"] == base.tokens * k
+        assert rp["send_demand"] == list(d["demand"]) and rp["send_count"] == list(d["demand"])
+    waves = O.wave_experts(base.local_experts, base.waves)
+    for r in range(R):
+        rv = ref["recv"][r]
+        seg = lay.seg_off[r]
+        n = int(seg[-1])
+        ids, _ = _decode_pools(lay.recv[r], L, act)
+        assert np.all(ids[n:] == -1), f"rank {r}: rows past the received ones"
+        for w, experts in enumerate(waves):
+            gcnt = host(lay.wave_count[r, w])
+            assert np.array_equal(gcnt, rv["count"][experts]), f"rank {r} wave {w}: counts"
+            gsrc = host(lay.row_src[r, w])
+            osrc = rv["row_src"][experts]
+            for j in range(len(experts)):
+                c = int(gcnt[j])
+                o = osrc[j, :c]
+                assert np.array_equal(gsrc[j, :c], seg[o // pool_rows] + o % pool_rows), \
+                    f"rank {r} wave {w} expert {j}: ragged row_src"
+        rp = reps[r]
+        assert rp["expert_arrivals"] == list(rv["arrivals"]) and rp["expert_kept"] == list(rv["arrivals"])
+        assert rp["recv_dropped"] == 0 and rp["recv_bad_ids"] == 0
+        ret = lay.ret[r].float().cpu().numpy().astype(np.float64) if act == "bf16" else lay.ret[r].cpu().numpy()
+        want_rows, got_rows = [], []
+        for s in range(R):
+            c = int(seg[s + 1] - seg[s])
+            want_rows.append(ref["ret"][r][s][:c])
+            got_rows.append(ret[seg[s]:seg[s] + c])
+        assert_stored_close(np.concatenate(got_rows), np.concatenate(want_rows), act, f"rank {r} returned rows")
+    for s in range(R):
+        assert_bar(host(lay.out[s]), ref["out"][s]["out_exact"], act, f"src {s} out")
+
+
 @pytest.mark.parametrize("tokens", [0, 1, 65])
 def test_all_ranks_ragged_and_empty(runner, tokens):
     sh = configs.with_tokens(configs.get("mini_bf16"), tokens)
@@ -347,3 +428,61 @@ def test_one_rank_full_size(runner, cfg):
     gout = host(lay.out[torch.as_tensor(tokens, device=lay.out.device)])
     ratio, raw = assert_bar(gout, out_exact, act, f"cfg{cfg} out (sampled tokens)")
     _say(f"[full-size] config {cfg}: bar ratio {ratio:.3g}, raw max|d|/rms {raw:.3g}")
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_one_rank_ragged_full_size(runner, cfg):
+    """The ragged dropless layer at one rank's real shape against the fixed-pool
+    layer with capacities fitted to the same counts (nothing drops in either):
+    the same routing, the same kept rows moved to the ragged row order, and the
+    same output bits (the fixed-pool layer's parity with the oracle at full size
+    is the test above)."""
+    sh = configs.get(cfg)
+    scap, _ = O.capacities(sh)
+    _say(f"[ragged full-size] config {cfg}")
+    inp = gen.generate(sh, seed=0, grid=True, send_cap=scap)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        drawn = dict(zip(range(sh.n_ranks), ex.map(inp["sources"], range(sh.n_ranks))))
+    # the counts (dispatch only, a receive cap no expert can reach)
+    probe = runner.RaggedOneRankLayer(replace(sh, layer="dispatch"), dict(inp, sources=drawn.__getitem__),
+                                      expert_rows=sh.n_ranks * sh.tokens)
+    probe.run()
+    rep = probe.drop_report()
+    pool_rows = max(max(rep["send_demand"]), max(probe.source_demand.values()))
+    expert_rows = max(rep["expert_arrivals"])
+    del probe
+    torch.cuda.empty_cache()
+    fit = configs.exact_fit(sh, pool_rows, expert_rows)
+    inp = gen.generate(fit, seed=0, grid=True, send_cap=pool_rows)
+    inp["sources"] = drawn.__getitem__
+    side = torch.cuda.Stream() if sh.layer == "full" else None
+    fixed = runner.OneRankLayer(fit, inp, gather="fused")
+    fixed.run(side=side)
+    torch.cuda.synchronize()
+    frep = fixed.drop_report()
+    names = ("logits", "idx", "w", "z", "slot_of", "row_src", "wave_count") + (("out",) if sh.layer == "full" else ())
+    want = {n: host(getattr(fixed, n)) for n in names}
+    del fixed
+    torch.cuda.empty_cache()
+    rag = runner.RaggedOneRankLayer(sh, inp, expert_rows)
+    rag.run(side=side)
+    torch.cuda.synchronize()
+    rrep = rag.drop_report()
+    _say(f"[ragged full-size] config {cfg}: pool rows {pool_rows}, expert rows {expert_rows}, "
+         f"received {rag.n_recv} rows")
+    assert frep["send_dropped"] == 0 and frep["recv_dropped"] == 0
+    assert rrep["send_dropped"] == 0 and rrep["recv_dropped"] == 0
+    assert rrep["send_demand"] == frep["send_demand"] and rrep["expert_arrivals"] == frep["expert_arrivals"]
+    for n in ("logits", "idx", "w", "z", "wave_count") + (("out",) if sh.layer == "full" else ()):
+        got = host(getattr(rag, n))
+        assert np.array_equal(got.view(np.uint8), want[n].view(np.uint8)), f"{n} differs from the fitted fixed pools"
+    so = want["slot_of"]
+    assert np.all(so >= 0)
+    assert np.array_equal(host(rag.slot_of), rag.own_off[so // pool_rows] + so % pool_rows), "ragged slot_of"
+    gsrc, wcnt = host(rag.row_src), want["wave_count"]
+    for w in range(sh.waves):
+        for j in range(wcnt.shape[1]):
+            c = int(wcnt[w, j])
+            o = want["row_src"][w, j, :c]
+            assert np.array_equal(gsrc[w, j, :c], rag.seg_off[o // pool_rows] + o % pool_rows), "ragged row_src"
