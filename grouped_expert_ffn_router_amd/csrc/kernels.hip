@@ -89,21 +89,23 @@ hipError_t launch_select_topk(const float* logits, int T, int E, int k, int32_t*
 
 // Rank of each lane's key among the lanes of this wave with the same key,
 // offset by the running count run[key] (wave-private LDS), which is advanced.
-// key < 0: no key.  All lanes of the wave must call this together.
-__device__ __forceinline__ int peel_rank(int key, int32_t* run) {
-  int rank = 0;
-  uint64_t active = __ballot(key >= 0);
-  const uint64_t lt = lanemask_lt();
-  while (active) {
-    const int leader = __builtin_ctzll(active);
-    const int kk = __shfl(key, leader);
-    const uint64_t m = __ballot(key == kk);
-    const int before = run[kk];
-    if (key == kk) rank = before + __popcll(m & lt);
-    if (lane_id() == leader) run[kk] = before + __popcll(m);
-    active &= ~m;
+// key < 0: no key; keys are below 2^kbits.  All lanes of the wave must call
+// this together.  The lanes holding the same key are found with one ballot
+// per key bit (a lane keeps the lanes that agree with it on every bit), so
+// the cost does not grow with the number of distinct keys in the wave; each
+// group's lowest lane advances run[key].
+__device__ __forceinline__ int peel_rank(int key, int32_t* run, int kbits) {
+  const bool valid = key >= 0;
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < kbits; ++b) {
+    const bool bit = valid && ((key >> b) & 1);
+    const uint64_t ones = __ballot(bit);
+    same &= bit ? ones : ~ones;
   }
-  return rank;
+  const uint64_t below = same & lanemask_lt();
+  const int before = valid ? run[key] : 0;
+  if (valid && below == 0) run[key] = before + __popcll(same);
+  return before + __popcll(below);
 }
 
 // Block-wide: rank 1024 keys (4 waves x 4 x 64) inside the chunk; write each
@@ -115,6 +117,8 @@ __device__ __forceinline__ void chunk_rank(GetKey get_key, int n, int KW, int nc
                                            int32_t* __restrict__ key_out) {
   for (int i = threadIdx.x; i < 4 * KW; i += 256) run_all[i] = 0;
   __syncthreads();
+  int kbits = 0;
+  while ((1 << kbits) < KW) ++kbits;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   int32_t* run = run_all + wave * KW;
   const int base = blockIdx.x * SCAN_CHUNK + wave * 256;
@@ -123,7 +127,7 @@ __device__ __forceinline__ void chunk_rank(GetKey get_key, int n, int KW, int nc
   for (int it = 0; it < 4; ++it) {
     const int i = base + it * 64 + lane;
     key[it] = i < n ? get_key(i) : -1;
-    rk[it] = peel_rank(key[it], run);
+    rk[it] = peel_rank(key[it], run, kbits);
   }
   __syncthreads();
 #pragma unroll
