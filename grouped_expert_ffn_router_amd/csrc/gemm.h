@@ -128,8 +128,7 @@ struct BKSeg {
 // store4_pair(ctx, u, gate[4], up[4]) for hidden units u..u+3.
 
 __device__ __forceinline__ uint2 pack_bf16x4(const float* v) {
-  return make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                    (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+  return make_uint2(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]));
 }
 
 // 4 consecutive activations at p (8-byte aligned for bf16 when full).
