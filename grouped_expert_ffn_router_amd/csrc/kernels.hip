@@ -436,25 +436,34 @@ hipError_t launch_wave_gather(const void* pools, int64_t src_stride, int64_t pro
   return hipGetLastError();
 }
 
-// One wave per receive row: a row of this wave's experts that did not fit
-// gets an all-zero return row.
+// A receive row of this wave's experts that did not fit gets an all-zero
+// return row.  One lane checks one row; the wave then zeroes its dropped rows
+// together (none, usually: the launch costs a quarter of a wave per 64 rows).
 __global__ void __launch_bounds__(256)
 zero_dropped_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict__ row_rank, int n_rows, int cap,
                     int rcap, int j0, int nj, char* __restrict__ ret, int64_t ret_src_stride, int64_t row_bytes) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n_rows) return;
-  const int j = row_j[row];
-  if (j < j0 || j >= j0 + nj || row_rank[row] < rcap) return;
-  const int s = row / cap, sl = row - s * cap;
-  uint4* dst = (uint4*)(ret + s * ret_src_stride + (int64_t)sl * row_bytes);
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  bool drop = false;
+  if (row < n_rows) {
+    const int j = row_j[row];
+    drop = j >= j0 && j < j0 + nj && row_rank[row] >= rcap;
+  }
+  uint64_t m = __ballot(drop);
+  const int base = row - lane_id();
   const int nchunk = (int)(row_bytes >> 4);
-  for (int c = lane_id(); c < nchunk; c += 64) dst[c] = make_uint4(0, 0, 0, 0);
+  while (m) {
+    const int r = base + __builtin_ctzll(m);
+    m &= m - 1;
+    const int s = r / cap, sl = r - s * cap;
+    uint4* dst = (uint4*)(ret + s * ret_src_stride + (int64_t)sl * row_bytes);
+    for (int c = lane_id(); c < nchunk; c += 64) dst[c] = make_uint4(0, 0, 0, 0);
+  }
 }
 
 hipError_t launch_zero_dropped(const int32_t* row_j, const int32_t* row_rank, int n_rows, int cap, int rcap, int j0,
                                int nj, void* ret, int64_t ret_src_stride, int64_t row_bytes, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_dropped_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, st, row_j, row_rank, n_rows, cap,
+  hipLaunchKernelGGL(zero_dropped_kernel, dim3((n_rows + 255) / 256), dim3(256), 0, st, row_j, row_rank, n_rows, cap,
                      rcap, j0, nj, (char*)ret, ret_src_stride, row_bytes);
   return hipGetLastError();
 }
