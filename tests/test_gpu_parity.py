@@ -486,3 +486,73 @@ def test_one_rank_ragged_full_size(runner, cfg):
             c = int(wcnt[w, j])
             o = want["row_src"][w, j, :c]
             assert np.array_equal(gsrc[w, j, :c], rag.seg_off[o // pool_rows] + o % pool_rows), "ragged row_src"
+
+
+@pytest.mark.parametrize("tokens,pattern", [(0, "uniform"), (1, "uniform"), (777, "uniform"), (777, "invalid"),
+                                             (1500, "one_destination")])
+def test_pack_ragged_direct(runner, tokens, pattern):
+    """moe_pack_ragged on chosen expert ids against its definition written out as a
+    loop: assignments visited in (t, i) order, destination e / X, the r-th one of
+    destination d at row send_off[d] + r, send_off the exclusive scan of the counts;
+    ids outside [0, E) get slot -1 and no row.  Covers an empty batch, ids that
+    no expert has, and every assignment on one destination (one long segment)."""
+    from grouped_expert_ffn_router_amd import binding as B
+    sh = configs.with_tokens(configs.get("mini_bf16"), tokens)
+    T, k, E, R, L = sh.tokens, sh.top_k, sh.n_experts, sh.n_ranks, sh.latent
+    X = E // R
+    rng = np.random.default_rng(17 + tokens)
+    if pattern == "one_destination":
+        idx = np.stack([rng.choice(X, k, replace=False) + 2 * X for _ in range(T)]) if T else np.zeros((0, k))
+    else:
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]) if T else np.zeros((0, k))
+    idx = idx.astype(np.int32).reshape(T, k)
+    if pattern == "invalid" and T:
+        bad = rng.random((T, k)) < 0.1
+        idx[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, E + 5)
+    _say(f"[pack ragged] tokens={T} pattern={pattern}")
+    dims = B.make_dims(sh)
+    _, _, prow = B.capacity(dims)
+    dev = "cuda"
+    z_host = gen.f32_to_bf16_bits_trunc(rng.standard_normal((T, L)).astype(np.float32)) if T else np.zeros((0, L), np.uint16)
+    z = torch.from_numpy(z_host.view(np.int16)).to(dev).view(torch.bfloat16) if T else \
+        torch.empty((0, L), dtype=torch.bfloat16, device=dev)
+    t_idx = torch.from_numpy(idx).to(dev)
+    rows = torch.full((max(T * k, 1), prow), 0x5A, dtype=torch.uint8, device=dev)
+    send_off = torch.full((R + 1,), -7, dtype=torch.int32, device=dev)
+    slot_of = torch.full((max(T, 1), k), -9, dtype=torch.int32, device=dev)
+    send_count = torch.full((R,), -5, dtype=torch.int32, device=dev)
+    ws = torch.zeros((B.workspace_size(dims),), dtype=torch.uint8, device=dev)
+    B.pack_ragged(dims, z, t_idx, rows, send_off, slot_of, send_count, ws)
+    torch.cuda.synchronize()
+    # the definition, as a loop
+    count = np.zeros(R, np.int64)
+    dest_rank = np.full((T, k), -1, np.int64)
+    for t in range(T):
+        for i in range(k):
+            e = int(idx[t, i])
+            if 0 <= e < E:
+                dest_rank[t, i] = count[e // X]
+                count[e // X] += 1
+    off = np.concatenate([[0], np.cumsum(count)])
+    want_slot = np.full((T, k), -1, np.int64)
+    for t in range(T):
+        for i in range(k):
+            if dest_rank[t, i] >= 0:
+                want_slot[t, i] = off[int(idx[t, i]) // X] + dest_rank[t, i]
+    assert np.array_equal(host(send_count), count), "send_count"
+    assert np.array_equal(host(send_off), off), "send_off"
+    if T:
+        assert np.array_equal(host(slot_of)[:T], want_slot), "slot_of"
+    rep = B.drop_stats(dims, ws, raise_on_bad_ids=False).as_dict()
+    assert rep["send_dropped"] == int((idx < 0).sum() + (idx >= E).sum()) and rep["send_kept"] == int(count.sum())
+    n = int(off[-1])
+    if n:
+        ids, vals = _decode_pools(rows[:n], L, sh.act)
+        ok = want_slot >= 0
+        assert np.array_equal(ids[want_slot[ok]], idx[ok]), "row ids"
+        tok = np.repeat(np.arange(T), k).reshape(T, k)
+        zf = gen.bf16_bits_to_f32(z_host).astype(np.float64)
+        assert np.array_equal(vals[want_slot[ok]], zf[tok[ok]]), "row payloads"
+    # rows past the written ones are left alone
+    tail = host(rows[n:]) if n < rows.shape[0] else np.zeros((0,), np.uint8)
+    assert np.all(tail == 0x5A), "rows past send_off[R] were written"
