@@ -245,7 +245,7 @@ const char* moe_last_error(void);
  * above is bracketed by two HIP events recorded on the stream it is launched
  * on, so the elapsed time between them is that kernel's duration on its own
  * stream.  Enabling adds two event records per launch; results are unchanged.
- * Labels: route_gemm, select_topk, send_rank, send_scan, pack, recv_rank,
+ * Labels: route_gemm, select_topk, send_rank, send_scan, ragged_offsets, pack, recv_rank,
  * recv_scan, recv_final, recv_place, wave_gather, expert_gate_up, expert_down,
  * zero_dropped, combine, shared_gate_up, up_shared_down, and the tail-split
  * fixups route_fixup, gate_up_fixup, down_fixup, up_fixup. */
