@@ -145,6 +145,9 @@ int derive(const moe_dims* d, Q* q) {
   if (bf16) {
     if (d->d_model % 64 || d->latent % 64 || d->expert_hidden % 64 || d->shared_hidden % 64)
       return fail(MOE_EINVAL, "bf16 layers need d_model, latent, expert_hidden, shared_hidden multiples of 64");
+    // the up-projection GEMM's K (latent plus the shared hidden units) picks its segment in float
+    if ((int64_t)d->latent + (int64_t)d->shared_experts * d->shared_hidden >= (1ll << 24))
+      return fail(MOE_EINVAL, "latent + shared_experts * shared_hidden must be below 2^24");
     if (d->n_experts % 4) return fail(MOE_EINVAL, "bf16 layers need n_experts to be a multiple of 4");
   } else if (d->latent % 8 || d->shared_hidden % 4) {
     // the combined [latent | shared hidden] rows are written with 16-byte stores
@@ -342,7 +345,7 @@ hipError_t up_and_shared_down(const Q& q, const void* ws2, const void* w_up, T* 
                               hipStream_t st) {
   const int64_t ldc = q.L + q.S * q.HS;
   ARows<T> a2{cat, ldc, 0, nullptr, (int)q.T};
-  BKSeg<T> b2{(const T*)w_up, q.L, (int)q.L, (const T*)ws2, q.HS, (int)q.HS, q.D * q.HS};
+  BKSeg<T> b2{(const T*)w_up, q.L, (int)q.L, (const T*)ws2, q.HS, (int)q.HS, q.D * q.HS, 1.0f / (float)q.HS};
   EStore<T> e2{(T*)out, q.D};
   if constexpr (sizeof(T) == 2)
     return gemm_bf16<false>("up_shared_down", "up_fixup", a2, b2, e2, (int)q.D, (int)ldc, q.T, true, 1, part, st);

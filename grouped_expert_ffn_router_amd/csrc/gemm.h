@@ -119,6 +119,23 @@ struct BKSeg {
     const int kk = k - k0, j = kk / k1;
     return b1 + j * stride1 + (int64_t)n * ld1 + (kk - j * k1);
   }
+  float inv_k1;  // 1 / k1 (0 when there are no k1 segments)
+  // The part of the address of B[n][k .. k+63] shared by every row, for k a
+  // multiple of 64 (k0 and k1 are too, so a K step stays inside one
+  // segment); k is uniform across the workgroup.  Branch-free, so that it
+  // sits inside the MFMA-interleaved K loop without splitting it: the
+  // segment index is floor((kk + 32) / k1), whose true value lies at least
+  // 32 / k1 from an integer, more than the float product's error for
+  // kk < 2^24 (K is checked against that on the host).
+  // Row n then adds n * ld0 in the first segment and n * ld1 in the others.
+  __device__ const T* kbase(int k, bool& first) const {
+    first = k < k0;
+    const int kk = k - k0;
+    const int j = __builtin_amdgcn_readfirstlane(first ? 0 : (int)((float)(kk + 32) * inv_k1));
+    const uint64_t seg = (uint64_t)(b1 + (int64_t)j * stride1 + (kk - j * k1));
+    const uint64_t lead = (uint64_t)(b0 + k), pick = first ? ~0ull : 0ull;  // a blend, not a branch
+    return (const T*)((lead & pick) | (seg & ~pick));
+  }
 };
 
 // ------------------------------------------------------------ epilogues
@@ -472,6 +489,18 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int groups, int tiles_n, int P, floa
     nb_row[d] = min(n0 + wave * RPW + d * 8 + lrow, N - 1);
     pb[d] = b.ptr(g, nb_row[d], gcola[d & 1]) - 512 * d;
   }
+  // K-concatenated B: each lane's row offsets in the first segment and in
+  // the others; a load adds the one its (uniform) K step needs.
+  // (Two arrays picked by a select: an array indexed by the segment would be
+  // a dynamically indexed private array.)
+  int64_t kso0[LB], kso1[LB];
+  if constexpr (B::KSEG) {
+#pragma unroll
+    for (int d = 0; d < LB; ++d) {
+      kso0[d] = (int64_t)nb_row[d] * b.ld0 + gcola[d & 1] - 512 * d;
+      kso1[d] = (int64_t)nb_row[d] * b.ld1 + gcola[d & 1] - 512 * d;
+    }
+  }
 
   const int frow = lane & 31, fhalf = lane >> 5;
   const int fswz = swz(frow);
@@ -506,7 +535,13 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int groups, int tiles_n, int P, floa
       gp = (const void*)(pa[dd] + k0);
       lp = s + wave * WBYTES;
     } else {
-      gp = (const void*)(B::KSEG ? b.ptr(g, nb_row[dd], k0 + gcola[dd & 1]) - 512 * dd : pb[dd] + k0);
+      if constexpr (B::KSEG) {
+        bool first;
+        const bf16_t* kb = b.kbase(k0, first);
+        gp = (const void*)(kb + (first ? kso0[dd] : kso1[dd]));
+      } else {
+        gp = (const void*)(pb[dd] + k0);
+      }
       lp = s + BM * ROW + wave * WBYTES;
     }
     auto l3 = (__attribute__((address_space(3))) void*)lp;
