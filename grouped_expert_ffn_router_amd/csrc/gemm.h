@@ -102,6 +102,14 @@ struct BGateUp {
   }
 };
 
+// Index of the k1-long segment holding K offset kk, for kk and k1 multiples
+// of 64 (inv_k1 = 1 / k1 in float): floor((kk + 32) / k1) has its true value
+// at least 32 / k1 away from an integer, more than the error of the float
+// product for kk < 2^24, so truncating the product is exact there.
+__host__ __device__ __forceinline__ int kseg_index(int kk, float inv_k1) {
+  return (int)((float)(kk + 32) * inv_k1);
+}
+
 // K-concatenated operand: k in [0, k0) from b0 (row n at b0 + n*ld0), then
 // consecutive segments of k1 from expert j of b1 (row n at b1 + j*stride1 + n*ld1).
 template <class T>
@@ -123,15 +131,13 @@ struct BKSeg {
   // The part of the address of B[n][k .. k+63] shared by every row, for k a
   // multiple of 64 (k0 and k1 are too, so a K step stays inside one
   // segment); k is uniform across the workgroup.  Branch-free, so that it
-  // sits inside the MFMA-interleaved K loop without splitting it: the
-  // segment index is floor((kk + 32) / k1), whose true value lies at least
-  // 32 / k1 from an integer, more than the float product's error for
-  // kk < 2^24 (K is checked against that on the host).
+  // sits inside the MFMA-interleaved K loop without splitting it (the
+  // segment index comes from kseg_index; K < 2^24 is checked on the host).
   // Row n then adds n * ld0 in the first segment and n * ld1 in the others.
   __device__ const T* kbase(int k, bool& first) const {
     first = k < k0;
     const int kk = k - k0;
-    const int j = __builtin_amdgcn_readfirstlane(first ? 0 : (int)((float)(kk + 32) * inv_k1));
+    const int j = __builtin_amdgcn_readfirstlane(first ? 0 : kseg_index(kk, inv_k1));
     const uint64_t seg = (uint64_t)(b1 + (int64_t)j * stride1 + (kk - j * k1));
     const uint64_t lead = (uint64_t)(b0 + k), pick = first ? ~0ull : 0ull;  // a blend, not a branch
     return (const T*)((lead & pick) | (seg & ~pick));

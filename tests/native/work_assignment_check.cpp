@@ -2,7 +2,9 @@
 // counts, every (output tile, K step) is computed by exactly one workgroup of
 // the launch grid, every tail part writes its own partial slot where the
 // fixup kernel looks for it, and tile numbers map one-to-one onto the tiles
-// that exist.  Exit status 0 on success; the first failure is printed.
+// that exist; and the float K-segment index of the concatenated B operand is
+// exact for 64-aligned offsets below 2^24.  Exit status 0 on success; the
+// first failure is printed.
 #include <stdio.h>
 #include <stdlib.h>
 #include <vector>
@@ -100,6 +102,22 @@ int main() {
     ++cases;
   }
   if (split_cases < 100) return fail("too few cases with a tail split", split_cases, cases);
-  printf("ok %d cases, %d with a tail split\n", cases, split_cases);
+  // The K-segment index of the concatenated B operand, computed in float:
+  // exact for every 64-aligned offset below 2^24 and 64-aligned segment length.
+  long seg_checks = 0;
+  for (int k1 = 64; k1 <= 65536; k1 += (k1 < 4096 ? 64 : 1088)) {
+    const float inv = 1.0f / (float)k1;
+    const int step = k1 <= 1024 ? 64 : 64 * 7;
+    for (int kk = 0; kk < (1 << 24); kk += step) {
+      ++seg_checks;
+      if (kseg_index(kk, inv) != kk / k1) return fail("K segment index", kk, k1);
+    }
+    for (int s = 1; (long)s * k1 < (1 << 24); ++s)  // both sides of every boundary
+      for (int kk = s * k1 - 64; kk <= s * k1; kk += 64) {
+        ++seg_checks;
+        if (kseg_index(kk, inv) != kk / k1) return fail("K segment boundary", kk, k1);
+      }
+  }
+  printf("ok %d cases, %d with a tail split, %ld K-segment offsets\n", cases, split_cases, seg_checks);
   return 0;
 }

@@ -4,7 +4,9 @@ Compiles tests/native/work_assignment_check.cpp against the library's GEMM
 header with hipcc (host code only) and runs it: for the layer's GEMM shapes
 and thousands of random tile counts, every (output tile, K step) is owned by
 exactly one workgroup of the launch grid and every tail part writes the
-partial slot the fixup kernel reads.
+partial slot the fixup kernel reads; and the float K-segment index of the
+up-projection GEMM's concatenated operand is exact for every 64-aligned
+offset below 2^24.
 """
 
 import os
