@@ -126,7 +126,8 @@ int moe_route(const moe_dims* dims, const void* x, const void* w_router, const v
  *   send_pools       R pools of send_cap rows of pool_stride_bytes each; pool d
  *                    starts at send_pools + d * dst_stride_bytes; row layout:
  *                    L act values, then the int32 global expert id (-1 for an
- *                    empty slot; an empty row's payload is left unwritten)
+ *                    empty slot; an empty row's payload is left unwritten),
+ *                    then zeros up to pool_stride_bytes
  *   slot_of          [T][k] int32 output: d * send_cap + slot, or -1 if dropped
  *   send_count       [R] int32 output: rows kept per destination */
 int moe_pack_pools(const moe_dims* dims, const void* z, const int32_t* topk_idx,
@@ -142,7 +143,8 @@ int moe_pack_pools(const moe_dims* dims, const void* z, const int32_t* topk_idx,
  * rows.  The send capacity factor in dims is not used.
  *   send_rows   [T*k][pool_stride_bytes]: the r-th row for destination d is
  *               row send_off[d] + r (L act values, then the int32 global
- *               expert id); rows past send_off[R] are left unwritten
+ *               expert id, then zeros up to pool_stride_bytes); rows past
+ *               send_off[R] are left unwritten
  *   send_off    [R+1] int32 output: exclusive scan of send_count; send_off[R]
  *               is the number of rows written
  *   slot_of     [T][k] int32 output: send_off[d] + r (a row index), or -1 for

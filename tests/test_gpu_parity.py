@@ -94,6 +94,8 @@ def _check_all_ranks(sh, inp, ref, lay, grid):
     assert (lay.scap, lay.rcap) == (scap, rcap)
     reps = lay.drop_reports()
     pool_ids, pool_rows = _decode_pools(lay.pools, L, act)           # [src][dst][cap]
+    es = 2 if act == "bf16" else 4
+    assert not lay.pools.cpu().numpy()[..., L * es + 4:].any(), "pool rows past the id are not zero"
     for s in range(R):
         d = ref["dispatch"][s]
         _check_routing(sh, d, host(lay.logits[s]), host(lay.idx[s]), host(lay.w[s]), grid, f"src {s}")
@@ -560,6 +562,7 @@ def test_pack_ragged_direct(runner, tokens, pattern):
         tok = np.repeat(np.arange(T), k).reshape(T, k)
         zf = gen.bf16_bits_to_f32(z_host).astype(np.float64)
         assert np.array_equal(vals[want_slot[ok]], zf[tok[ok]]), "row payloads"
+        assert not host(rows[:n])[:, L * 2 + 4:].any(), "rows past the id are not zero"
     # rows past the written ones are left alone
     tail = host(rows[n:]) if n < rows.shape[0] else np.zeros((0,), np.uint8)
     assert np.all(tail == 0x5A), "rows past send_off[R] were written"
