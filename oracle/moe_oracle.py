@@ -328,9 +328,13 @@ def shared_hidden(x, ws13, shared_hidden_width, act):
     """Hidden activations of the always-on shared experts: [T][S*HS].
 
     [P1 §二]: 2 shared experts stay local and process every token, outside
-    the routed path.  Reading: SwiGLU experts on the 6,144-wide input.
+    the routed path.  Reading: SwiGLU experts on the 6,144-wide input.  With
+    no shared experts (S = 0) the hidden rows are empty and the shared term
+    of the output is zero.
     """
     X = f64(x)
+    if ws13.shape[0] == 0:
+        return np.zeros((X.shape[0], 0))
     return np.concatenate([swiglu_hidden(X, ws13[j], shared_hidden_width, act)
                            for j in range(ws13.shape[0])], axis=1)
 

@@ -283,6 +283,19 @@ def test_all_ranks_ragged_and_empty(runner, tokens):
     _check_all_ranks(sh, inp, ref, lay, True)
 
 
+def test_all_ranks_no_shared_experts(runner):
+    """A layer with no shared experts (S = 0): the shared call does nothing and the
+    output is the routed term alone."""
+    sh = replace(configs.get("mini_bf16"), name="mini_bf16_noshared", shared_experts=0)
+    _say("[all-ranks] mini_bf16 shared_experts=0")
+    inp = gen.generate(sh, seed=6, grid=True)
+    ref = O.layer_all_ranks(sh, inp)
+    lay = runner.AllRanksLayer(sh, inp)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, True)
+
+
 def test_all_logits_equal_degenerate_router(runner):
     """W_r = 0: every token picks experts 0..k-1 with weight 1/k; most assignments drop."""
     sh = configs.get("mini_bf16")

@@ -321,6 +321,22 @@ def test_no_drop_limit_equals_textbook_moe():
             np.testing.assert_allclose(res["out"][s]["out_exact"][t], ref, rtol=1e-9, atol=1e-12)
 
 
+def test_no_shared_experts_is_the_routed_textbook_layer():
+    """S = 0 (a layer without the always-on shared experts): the output is the
+    routed term alone, the textbook MoE evaluated token by token."""
+    from dataclasses import replace
+    sh = replace(configs.get("mini_f32"), shared_experts=0, send_num=100000, recv_num=100000)
+    inp = gen.generate(sh, seed=9)
+    res = O.layer_all_ranks(sh, inp)
+    rng = np.random.default_rng(1)
+    for s in range(sh.n_ranks):
+        d = res["dispatch"][s]
+        assert res["out"][s]["hs"].shape == (sh.tokens, 0)
+        for t in rng.choice(sh.tokens, 6, replace=False):
+            ref = _textbook_token(sh, inp, s, t, d["idx"][t], d["w"][t])
+            np.testing.assert_allclose(res["out"][s]["out_exact"][t], ref, rtol=1e-9, atol=1e-12)
+
+
 def test_a_fully_dropped_token_gets_the_shared_path_only():
     from dataclasses import replace
     sh = replace(configs.get("mini_f32"), send_num=1, send_den=100)   # tiny send pools
