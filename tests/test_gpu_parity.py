@@ -296,6 +296,22 @@ def test_all_ranks_no_shared_experts(runner):
     _check_all_ranks(sh, inp, ref, lay, True)
 
 
+@pytest.mark.parametrize("gather", ["fused", "buffer"])
+def test_all_ranks_top1_one_expert_per_rank(runner, gather):
+    """The smallest structure the method has: top-1 routing, one expert per rank,
+    a single wave; the send cap binds."""
+    sh = replace(configs.get("mini_bf16"), name="mini_bf16_top1", n_experts=8, n_ranks=8, top_k=1, waves=1,
+                 tokens=200)
+    _say(f"[all-ranks] mini_bf16 top_k=1 one expert per rank, gather={gather}")
+    inp = gen.generate(sh, seed=4, grid=True)
+    ref = O.layer_all_ranks(sh, inp)
+    assert ref["ledger"]["send_dropped"].sum() > 0
+    lay = runner.AllRanksLayer(sh, inp, gather=gather)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, True)
+
+
 def test_all_logits_equal_degenerate_router(runner):
     """W_r = 0: every token picks experts 0..k-1 with weight 1/k; most assignments drop."""
     sh = configs.get("mini_bf16")
