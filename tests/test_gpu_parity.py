@@ -312,6 +312,22 @@ def test_all_ranks_top1_one_expert_per_rank(runner, gather):
     _check_all_ranks(sh, inp, ref, lay, True)
 
 
+def test_all_ranks_max_top_k(runner):
+    """top_k = 32, the largest the library takes: the combine sums its rows in
+    several batches of 8 and the per-token slot arrays are full; both caps
+    bind (factors 0.95 and 0.92)."""
+    sh = replace(configs.get("mini_bf16"), name="mini_bf16_k32", n_experts=64, n_ranks=8, top_k=32, waves=2,
+                 tokens=150, send_num=95, recv_num=92)
+    _say("[all-ranks] mini_bf16 top_k=32")
+    inp = gen.generate(sh, seed=2, grid=True)
+    ref = O.layer_all_ranks(sh, inp)
+    assert ref["ledger"]["send_dropped"].sum() > 0 and ref["ledger"]["recv_dropped"].sum() > 0
+    lay = runner.AllRanksLayer(sh, inp)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, True)
+
+
 def test_all_logits_equal_degenerate_router(runner):
     """W_r = 0: every token picks experts 0..k-1 with weight 1/k; most assignments drop."""
     sh = configs.get("mini_bf16")
