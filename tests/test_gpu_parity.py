@@ -328,6 +328,22 @@ def test_all_ranks_max_top_k(runner):
     _check_all_ranks(sh, inp, ref, lay, True)
 
 
+def test_all_ranks_many_ranks(runner):
+    """256 ranks of 2 experts, every one emulated: 257 send keys (9 key bits in
+    the wave-ballot ranking instead of the 7 of 64 ranks) and a send cap of one
+    row per pool, so most assignments drop at send and many at receive."""
+    sh = replace(configs.get("mini_bf16"), name="mini_bf16_r256", n_experts=512, n_ranks=256, top_k=4, waves=2,
+                 tokens=24, d_model=128, latent=64, expert_hidden=64, shared_experts=1, shared_hidden=64)
+    _say("[all-ranks] 256 ranks")
+    inp = gen.generate(sh, seed=3, grid=True)
+    ref = O.layer_all_ranks(sh, inp)
+    assert ref["send_cap"] == 1 and ref["ledger"]["recv_dropped"].sum() > 0
+    lay = runner.AllRanksLayer(sh, inp)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, True)
+
+
 def test_all_logits_equal_degenerate_router(runner):
     """W_r = 0: every token picks experts 0..k-1 with weight 1/k; most assignments drop."""
     sh = configs.get("mini_bf16")
