@@ -344,6 +344,24 @@ def test_all_ranks_many_ranks(runner):
     _check_all_ranks(sh, inp, ref, lay, True)
 
 
+@pytest.mark.parametrize("gather", ["fused", "buffer"])
+def test_all_ranks_many_local_experts(runner, gather):
+    """64 local experts per rank (the library's maximum) in 4 waves of 16: 65
+    receive keys in the ranking, 16 expert groups per grouped GEMM, receive
+    drops at a receive factor of 0.9."""
+    sh = replace(configs.get("mini_bf16"), name="mini_bf16_x64", n_experts=128, n_ranks=2, top_k=4, waves=4,
+                 tokens=300, d_model=256, latent=128, expert_hidden=64, shared_experts=1, shared_hidden=64,
+                 recv_num=90)
+    _say(f"[all-ranks] 64 local experts, gather={gather}")
+    inp = gen.generate(sh, seed=8, grid=True)
+    ref = O.layer_all_ranks(sh, inp)
+    assert ref["ledger"]["recv_dropped"].sum() > 0
+    lay = runner.AllRanksLayer(sh, inp, gather=gather)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, True)
+
+
 def test_all_logits_equal_degenerate_router(runner):
     """W_r = 0: every token picks experts 0..k-1 with weight 1/k; most assignments drop."""
     sh = configs.get("mini_bf16")
