@@ -12,7 +12,53 @@ namespace moe {
 
 // ------------------------------------------------------------------ top-k
 
-// One wave per token: k rounds of a wave-wide (value desc, index asc) argmax.
+// Order-preserving 64-bit key of (logit, expert): a larger logit first, then
+// the lower expert index; -0.0 is folded into +0.0 so that equal logits give
+// equal high halves.  Padding entries get key 0, below every real key.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+}
+
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// DPP move of a 64-bit value (two 32-bit halves) with control CTRL.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Largest key of the wave, in every lane: rotations by 8, 4, 2 and 1 lanes
+// inside each 16-lane row (DPP row_ror) give every lane its row's maximum,
+// then the four rows' maxima are read as scalars.  No LDS round trip.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  uint64_t t;
+  t = dpp_u64<0x128>(k); k = t > k ? t : k;
+  t = dpp_u64<0x124>(k); k = t > k ? t : k;
+  t = dpp_u64<0x122>(k); k = t > k ? t : k;
+  t = dpp_u64<0x121>(k); k = t > k ? t : k;
+  const uint64_t r0 = readlane_u64(k, 0), r1 = readlane_u64(k, 16), r2 = readlane_u64(k, 32),
+                 r3 = readlane_u64(k, 48);
+  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
+}
+
+// One wave per token: k rounds of a wave-wide argmax over (logit desc,
+// expert asc) keys; lane i < k keeps the i-th pick.  Weights: softmax over
+// the k picked logits, relative to the largest.
 template <int EPL>
 __global__ void __launch_bounds__(256)
 select_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx,
@@ -21,43 +67,29 @@ select_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int32_
   const int lane = lane_id();
   if (t >= T) return;
   const float* row = logits + (int64_t)t * E;
-  float v[EPL];
-  uint32_t taken = 0;
+  uint64_t key[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? row[e] : 0.f;
-    if (e >= E) taken |= 1u << j;
+    key[j] = e < E ? topk_key(row[e], e) : 0ull;
   }
   float my_v = 0.f, v0 = 0.f;
   int my_i = 0;
   for (int r = 0; r < k; ++r) {
-    float bv = 0.f;
-    int bi = 0x7fffffff;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const int e = lane + 64 * j;
-      if (!((taken >> j) & 1u) && (bi == 0x7fffffff || v[j] > bv || (v[j] == bv && e < bi))) {
-        bv = v[j];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      const bool better = (oi != 0x7fffffff) && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
-      if (better) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (r == 0) v0 = bv;
+    for (int j = 1; j < EPL; ++j) best = key[j] > best ? key[j] : best;
+    best = wave_max_key(best);
+    const int e = (int)~(uint32_t)best;
+    const float v = topk_key_value(best);
+    if (r == 0) v0 = v;
     if (lane == r) {
-      my_v = bv;
-      my_i = bi;
+      my_v = v;
+      my_i = e;
     }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j == e) key[j] = 0ull;
   }
   float ex = lane < k ? expf(my_v - v0) : 0.f;
   float sum = ex;

@@ -51,10 +51,11 @@ def _decode_pools(pools_u8, L, act):
     es = 2 if act == "bf16" else 4
     ids = np.ascontiguousarray(a[..., L * es:L * es + 4]).view(np.int32)[..., 0]
     pay = np.ascontiguousarray(a[..., :L * es])
-    if act == "bf16":
-        vals = gen.bf16_bits_to_f32(pay.view(np.uint16)).astype(np.float64)
-    else:
-        vals = pay.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):   # never-written payloads of empty rows may hold NaN bits
+        if act == "bf16":
+            vals = gen.bf16_bits_to_f32(pay.view(np.uint16)).astype(np.float64)
+        else:
+            vals = pay.view(np.float32).astype(np.float64)
     return ids, vals
 
 
