@@ -363,6 +363,22 @@ def test_all_ranks_many_local_experts(runner, gather):
     _check_all_ranks(sh, inp, ref, lay, True)
 
 
+@pytest.mark.parametrize("n_experts,n_ranks", [(1024, 16), (2048, 32)])
+def test_all_ranks_many_experts(runner, n_experts, n_ranks):
+    """1024 and 2048 experts (the library's maximum; 16 and 32 router logits
+    per lane in the top-k selection), 64 per rank in 4 waves."""
+    sh = replace(configs.get("mini_bf16"), name=f"mini_bf16_e{n_experts}", n_experts=n_experts, n_ranks=n_ranks,
+                 top_k=8, waves=4, tokens=40, d_model=128, latent=64, expert_hidden=64, shared_experts=1,
+                 shared_hidden=64)
+    _say(f"[all-ranks] {n_experts} experts")
+    inp = gen.generate(sh, seed=10, grid=True)
+    ref = O.layer_all_ranks(sh, inp)
+    lay = runner.AllRanksLayer(sh, inp)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, True)
+
+
 def test_all_logits_equal_degenerate_router(runner):
     """W_r = 0: every token picks experts 0..k-1 with weight 1/k; most assignments drop."""
     sh = configs.get("mini_bf16")
