@@ -1,0 +1,42 @@
+/* The C ABI used from plain C (no C++, no HIP headers): include/moe.h must
+ * compile as C11, and the host-only entry points and the argument checks
+ * (which reject bad calls before any HIP call) must work from C.
+ * Prints "ok" and exits 0 on success; the first failure is printed. */
+#include <stdio.h>
+#include <string.h>
+
+#include "moe.h"
+
+static int fail(const char* what) {
+  printf("FAIL: %s (last error: %s)\n", what, moe_last_error());
+  return 1;
+}
+
+int main(void) {
+  /* the 4K-context layer of one rank: 8192 tokens, 6144 -> 3072 latent, 384
+     experts over 64 ranks, top-8, 3 waves, expert hidden 1536, 2 shared
+     experts of hidden 1536, factors 1.10 and 1.15 */
+  moe_dims d = {8192, 6144, 3072, 384, 8, 64, 3, 1536, 2, 1536, 0, MOE_ACT_BF16, 110, 100, 115, 100};
+  int64_t send_cap = 0, recv_cap = 0, stride = 0;
+  if (moe_capacity(&d, &send_cap, &recv_cap, &stride) != MOE_OK) return fail("moe_capacity");
+  /* ceil(1.10 * 8192 * 8 / 64) = 1127; ceil(1.15 * 64 * 8192 * 8 / 384) = 12562;
+     a row is 6144 bytes of bf16 and the 4-byte id, padded to 128 bytes */
+  if (send_cap != 1127 || recv_cap != 12562 || stride != 6272) return fail("capacities");
+  size_t ws = 0;
+  if (moe_workspace_size(&d, &ws) != MOE_OK || ws == 0 || ws % 256) return fail("moe_workspace_size");
+
+  moe_dims bad = d;
+  bad.n_experts = 385; /* not a multiple of the rank count */
+  if (moe_capacity(&bad, NULL, NULL, NULL) != MOE_EINVAL || strlen(moe_last_error()) == 0)
+    return fail("bad dims accepted");
+  bad = d;
+  bad.act_dtype = 7;
+  if (moe_workspace_size(&bad, &ws) != MOE_EDTYPE) return fail("bad act_dtype accepted");
+  /* a NULL input is refused before any launch */
+  if (moe_route(&d, NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL) != MOE_EINVAL)
+    return fail("NULL input accepted");
+  if (strstr(moe_last_error(), "NULL") == NULL) return fail("error message");
+  printf("ok send_cap=%lld recv_cap=%lld stride=%lld workspace=%zu\n", (long long)send_cap, (long long)recv_cap,
+         (long long)stride, ws);
+  return 0;
+}

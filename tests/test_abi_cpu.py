@@ -110,3 +110,23 @@ def test_null_and_misaligned_pointers_are_rejected_before_any_launch():
     with pytest.raises(B.MoeError) as e:
         B.pack_ragged(d, 256, 256, 256, 258, 256, 256, 256, stream=0)
     assert e.value.code == B.MOE_EALIGN
+
+
+def test_header_compiles_as_c_and_the_host_entry_points_work_from_c(tmp_path):
+    """include/moe.h is plain C11 (no C++ or HIP types), and a C program linked
+    against libmoe.so gets the 4K-context capacities and the argument errors."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    B.lib()  # raises if the library was not built
+    pkg = os.path.join(ROOT, "grouped_expert_ffn_router_amd")
+    exe = tmp_path / "abi_c"
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "native", "abi_c_check.c"), "-L", pkg, "-lmoe", f"-Wl,-rpath,{pkg}",
+           "-o", str(exe)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout[-3000:]
+    out = subprocess.run([str(exe)], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=120)
+    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout[-2000:]
