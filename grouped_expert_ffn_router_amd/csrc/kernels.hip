@@ -1,9 +1,12 @@
 // Routing, slot assignment and row-movement kernels of libmoe (gfx950).
 //
+// Top-k selection: one wave per token, k rounds of a wave-wide maximum over
+// order-preserving (logit, expert) keys, reduced with DPP and lane reads.
 // Slot assignment is a deterministic two-pass scan: one 256-thread block
-// ranks SCAN_CHUNK keys with wave64 ballots (equal keys are peeled one value
-// at a time: ballot -> popcount of lower lanes), then one block per key
-// value scans the per-chunk counts.  No atomics.
+// ranks SCAN_CHUNK keys with wave64 ballots (the lanes holding the same key
+// are found with one ballot per key bit, then a popcount of the lower
+// lanes), then one block per key value scans the per-chunk counts.  No
+// atomics.
 
 #include "moe_common.h"
 #include "moe_internal.h"
