@@ -150,7 +150,19 @@ def cpu_baseline(cfg, seed, tokens):
              f"the {base.name} recipe at {tokens} tokens per rank (send pools of {scap} rows)")
     return {"value": tokens * sh.top_k / dt, "unit": "assignments/s", "cores": threads, "kind": "oracle",
             "sample": f"{scope}: {what} of one rank in the float64 oracle (seed {seed}), input generation "
-                      f"excluded, one run of {dt:.1f} s"}
+                      f"excluded, one run of {dt:.1f} s",
+            "host": {"cpu_model": _cpu_model(), "logical_cpus": os.cpu_count()}}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 SWEEP_FACTORS = [(110, 115), (100, 115), (125, 115), (150, 115), (110, 100), (110, 130), (110, 150)]
