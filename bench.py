@@ -21,7 +21,8 @@ Prints ONE JSON line with, besides the contract fields:
 
 Options: --steps K --warmup W --config {2,3,4,5,6} --gather {fused,buffer} --streams {1,2}
 --sweep-capacity (one line per capacity-factor point instead of the benchmark line),
---dropless (capacities fitted to the exchanged counts against the fixed factors)
+--dropless (capacities fitted to the exchanged counts against the fixed factors),
+--vendor-gemm (torch's bf16 matmul on the layer's GEMM shapes, a reference point for the GEMM core)
 --no-cpu-baseline --cpu-tokens N --seed S.  --gpus N > 1 exits: the benchmark
 measures one GPU.
 """
@@ -69,6 +70,10 @@ def parse():
                          "exchanged counts (no drops) against the fixed factors, one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="instead of the benchmark line: torch's bf16 matmul (the vendor GEMM library) on the "
+                         "layer's GEMM shapes with N(0,1) operands, one JSON line per shape (a reference point "
+                         "for the GEMM core, to be profiled with the same counters)")
     return ap.parse_args()
 
 
@@ -166,6 +171,35 @@ def _cpu_model():
 
 
 SWEEP_FACTORS = [(110, 115), (100, 115), (125, 115), (150, 115), (110, 100), (110, 130), (110, 150)]
+
+
+VENDOR_SHAPES = [(22528, 3072, 3072), (8192, 6144, 6144), (8192, 6144, 3072), (8192, 3456, 6144)]
+
+
+def vendor_gemm(args):
+    """torch.matmul in bf16 (the vendor library) on M x N x K shapes of the layer:
+    one expert wave's gate/up rows as one dense GEMM, the shared gate/up, the
+    up-projection + shared down, the route GEMM.  B is a transposed view of an
+    [N][K] matrix (2-D matmul, no batching)."""
+    import torch
+    torch.manual_seed(args.seed)
+    for M, N, K in VENDOR_SHAPES:
+        a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        b = torch.randn(N, K, device="cuda").to(torch.bfloat16)
+        bt = b.t()
+        for _ in range(args.warmup):
+            c = a @ bt
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            c = a @ bt
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        print(json.dumps({"vendor_gemm": "torch.matmul bf16", "M": M, "N": N, "K": K, "ms": ms,
+                          "tflops": 2 * M * N * K / (ms * 1e-3) / 1e12}), flush=True)
+        del a, b, bt, c
 
 
 def capacity_sweep(args):
@@ -320,6 +354,9 @@ def main():
         return
     if args.dropless:
         dropless(args)
+        return
+    if args.vendor_gemm:
+        vendor_gemm(args)
         return
     import torch
     from workload import configs, gen
