@@ -468,6 +468,13 @@ def test_one_rank_full_size(runner, cfg):
         lay.run()
         torch.cuda.synchronize()
         assert np.array_equal(host(lay.out).view(np.uint8), out2.view(np.uint8)), "two streams vs one"
+        # back-to-back steps as the benchmark times them (no synchronisation between
+        # them): a step's shared experts and waves must not overtake the previous
+        # step's combine
+        for _ in range(3):
+            lay.run(side=side)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(lay.out).view(np.uint8), out2.view(np.uint8)), "back-to-back steps"
         del out2
     rep = lay.drop_report()
     r = inp["receiver"]
