@@ -313,7 +313,7 @@ __host__ __device__ __forceinline__ void tile_coords(const A& a, int groups, int
     if (t < mt * tiles_n) break;
     t -= mt * tiles_n;
   }
-  constexpr int GROUP_M = 8;
+  constexpr int GROUP_M = 4;  // 32 tiles of an XCD at once: 4 tile rows x 8 tile columns
   const int width = GROUP_M * tiles_n;
   const int gid = t / width, first_m = gid * GROUP_M;
   const int gsz = mt - first_m < GROUP_M ? mt - first_m : GROUP_M;
@@ -558,8 +558,8 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int groups, int tiles_n, int P, floa
       default: __builtin_amdgcn_global_load_lds(gp, l3, 16, 3072, 0); break;
     }
   };
-  auto mma1 = [&](const Frags& f, int q) {
-    const int i = q / FN, j = q % FN;
+  auto mma1 = [&](const Frags& f, int q) {  // B fragment j held for FM consecutive MFMAs
+    const int j = q / FM, i = q % FM;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
   Frags F[2];  // substep ks computes on F[ks & 1] while F[(ks + 1) & 1] is read
