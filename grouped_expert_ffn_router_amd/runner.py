@@ -379,7 +379,9 @@ class AllRanksLayer:
         self.send_count = torch.empty((R, R), dtype=torch.int32, device=dev)
         self.row_src = torch.empty((R, W, WX, self.rcap), dtype=torch.int32, device=dev)
         self.wave_count = torch.empty((R, W, WX), dtype=torch.int32, device=dev)
-        self.wave_buf = torch.empty((WX, self.rcap, L), dtype=act, device=dev) if gather == "buffer" else None
+        # "buffer" gather: one wave buffer per (rank, wave), all kept for inspection
+        self.wave_buf = (torch.empty((R, W, WX, self.rcap, L), dtype=act, device=dev) if gather == "buffer"
+                         else None)
         self.ret = torch.zeros((R, R, self.scap, L), dtype=act, device=dev)                     # [recv][src]
         self.out = torch.empty((R, T, D), dtype=act, device=dev)
         self.ws = [torch.empty((B.workspace_size(self.dims[0]),), dtype=torch.uint8, device=dev)
@@ -403,9 +405,10 @@ class AllRanksLayer:
             recv_view = self.pools[0, r]                 # pool from source s at + s * R * pool_bytes
             B.recv_rank(d, recv_view, R * pool_bytes, self.ws[r], stream)
             for w in range(sh.waves):
-                B.recv_waves(d, recv_view, R * pool_bytes, w, self.wave_buf, self.row_src[r, w],
+                wb = None if self.wave_buf is None else self.wave_buf[r, w]
+                B.recv_waves(d, recv_view, R * pool_bytes, w, wb, self.row_src[r, w],
                              self.wave_count[r, w], self.ws[r], stream)
-                B.expert_gemm(d, w, self.wave_buf, recv_view, R * pool_bytes, self.row_src[r, w],
+                B.expert_gemm(d, w, wb, recv_view, R * pool_bytes, self.row_src[r, w],
                               self.wave_count[r, w], self.w13[r * X:(r + 1) * X], self.w2[r * X:(r + 1) * X],
                               self.ret[r], self.scap * L * esize, self.ws[r], stream)
         for s in range(R):

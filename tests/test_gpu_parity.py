@@ -126,6 +126,14 @@ def _check_all_ranks(sh, inp, ref, lay, grid):
             gcnt = host(lay.wave_count[r, w])
             assert np.array_equal(gcnt, rv["count"][experts]), f"rank {r} wave {w}: counts"
             assert np.array_equal(gsrc, rv["row_src"][experts]), f"rank {r} wave {w}: row_src"
+            if getattr(lay, "wave_buf", None) is not None:
+                # the wave gather (a plain copy of the GPU's own pool rows): exact,
+                # rows past each expert's count are left unwritten
+                want = O.wave_buffer(pool_rows[:, r], rv, experts, rcap)
+                got = host(lay.wave_buf[r, w])
+                for a, j in enumerate(experts):
+                    n = int(rv["count"][j])
+                    assert np.array_equal(got[a, :n], want[a, :n]), f"rank {r} wave {w} expert {j}: wave buffer"
         rp = reps[r]
         assert rp["expert_arrivals"] == list(rv["arrivals"]) and rp["expert_kept"] == list(rv["count"])
         assert rp["recv_dropped"] == rv["recv_dropped"].sum() and rp["recv_bad_ids"] == 0

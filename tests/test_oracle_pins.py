@@ -282,14 +282,19 @@ def test_waves_partition_the_local_experts():
 # ------------------------------------------------------------ whole layer
 
 
-def _textbook_token(shape, inp, s, t, idx, w):
-    """Dense MoE formula for one token (no capacities), fp64, with the layer's rounding points."""
+def _textbook_token(shape, inp, s, t, idx, w, kept=None):
+    """Dense MoE formula for one token, fp64, with the layer's rounding points.
+    ``kept[i]`` False leaves assignment i out of the routed sum (dropped at
+    either side: it contributes nothing and the other weights stay as they
+    are); None keeps all k (no capacities)."""
     act, H, HS = shape.act, shape.expert_hidden, shape.shared_hidden
     x = gen.to_f32(inp["x"][s][t]).astype(np.float64)
     Wd = gen.to_f32(inp["w_down"]).astype(np.float64)
     z = O.round_act(np.array([sum(x[q] * Wd[m, q] for q in range(x.size)) for m in range(Wd.shape[0])]), act)
     c = np.zeros(shape.latent)
     for i in range(shape.top_k):
+        if kept is not None and not kept[i]:
+            continue
         e = idx[i]
         W1 = gen.to_f32(inp["w13"][e][:H]).astype(np.float64)
         W3 = gen.to_f32(inp["w13"][e][H:]).astype(np.float64)
@@ -358,6 +363,114 @@ def test_a_fully_dropped_token_gets_the_shared_path_only():
     assert hit > 0
 
 
+def _brute_kept(idx_by_src, X, R, scap, rcap):
+    """Kept flag of every assignment of every source, by enumeration.
+
+    Send side: (t, i) is kept iff fewer than scap earlier assignments of its
+    source (in (t, i) order) go to the same destination; its slot is that
+    count.  Receive side: rank r visits sources in order and slots in order;
+    a row is kept iff fewer than rcap earlier visited rows carry an expert of
+    the same local index.  Returns (send_kept, recv_kept) as [R][T][k] bools."""
+    n_src = len(idx_by_src)
+    T, k = idx_by_src[0].shape
+    slot = np.full((n_src, T, k), -1, dtype=np.int64)
+    for s in range(n_src):
+        used = [0] * R
+        for t in range(T):
+            for i in range(k):
+                d = int(idx_by_src[s][t, i]) // X
+                if used[d] < scap:
+                    slot[s, t, i] = used[d]
+                used[d] += 1
+    recv_kept = np.zeros((n_src, T, k), dtype=bool)
+    for r in range(R):
+        seen = [0] * X
+        for s in range(n_src):
+            # the rows of pool (s -> r) in slot order
+            rows = sorted((slot[s, t, i], t, i) for t in range(T) for i in range(k)
+                          if slot[s, t, i] >= 0 and int(idx_by_src[s][t, i]) // X == r)
+            for _, t, i in rows:
+                j = int(idx_by_src[s][t, i]) - X * r
+                recv_kept[s, t, i] = seen[j] < rcap
+                seen[j] += 1
+    return slot >= 0, recv_kept
+
+
+def _recv_drop_case(seed=12):
+    """mini_f32 with send pools no token overfills and a receive cap of 0.7 of
+    the balanced load, so that only the receive cap drops."""
+    from dataclasses import replace
+    sh = replace(configs.get("mini_f32"), send_num=100000, recv_num=70)
+    return sh, gen.generate(sh, seed=seed)
+
+
+def test_receive_dropped_assignment_contributes_nothing():
+    """[P1 section 四]: a dropped assignment is not a dropped token.  Per token,
+    by brute force: with a receive cap that binds, every token gets exactly its
+    routed terms that survive both caps (weights not renormalised) plus the
+    shared path; the returned row of a receive-dropped assignment is zero."""
+    sh, inp = _recv_drop_case()
+    res = O.layer_all_ranks(sh, inp)
+    scap, rcap = res["send_cap"], res["recv_cap"]
+    X, R = sh.local_experts, sh.n_ranks
+    idx = [res["dispatch"][s]["idx"] for s in range(R)]
+    send_kept, recv_kept = _brute_kept(idx, X, R, scap, rcap)
+    assert send_kept.all(), "the send pools are sized so that nothing drops at send"
+    assert (~recv_kept).sum() > 20, "the receive cap must bind"
+    checked = 0
+    for s in range(R):
+        d = res["dispatch"][s]
+        hit = np.flatnonzero(~recv_kept[s].all(axis=1))
+        for t in hit[:8]:
+            ref = _textbook_token(sh, inp, s, t, d["idx"][t], d["w"][t], kept=recv_kept[s, t])
+            np.testing.assert_allclose(res["out"][s]["out_exact"][t], ref, rtol=1e-9, atol=1e-12)
+            checked += 1
+            for i in np.flatnonzero(~recv_kept[s, t]):
+                dest, sl = divmod(int(d["slot_of"][t, i]), scap)
+                assert not np.any(res["ret"][dest][s, sl]), "a receive-dropped row returned nonzero values"
+        # and a token that lost nothing is the plain textbook token
+        whole = np.flatnonzero(recv_kept[s].all(axis=1))
+        t = whole[0]
+        ref = _textbook_token(sh, inp, s, t, d["idx"][t], d["w"][t])
+        np.testing.assert_allclose(res["out"][s]["out_exact"][t], ref, rtol=1e-9, atol=1e-12)
+    assert checked >= 2 * R
+
+
+def _brute_wave_buffer(pool_ids, pool_rows, my_rank, X, experts, rcap):
+    """Wave buffer by a plain walk over (source, slot): row q of expert j is the
+    q-th row (q < rcap) that carries expert X*my_rank + j."""
+    n_src, cap, L = pool_rows.shape
+    buf = np.zeros((len(experts), rcap, L))
+    for a, j in enumerate(experts):
+        q = 0
+        for s in range(n_src):
+            for sl in range(cap):
+                if pool_ids[s, sl] == X * my_rank + j:
+                    if q < rcap:
+                        buf[a, q] = pool_rows[s, sl]
+                    q += 1
+    return buf
+
+
+def test_wave_buffer_by_enumeration():
+    """[P1 section 二]: each wave holds its experts' received rows in buffers of
+    one shape; rows in arrival order, at most recv_cap per expert."""
+    sh, inp = _recv_drop_case(seed=13)
+    res = O.layer_all_ranks(sh, inp)
+    scap, rcap, X, R = res["send_cap"], res["recv_cap"], sh.local_experts, sh.n_ranks
+    assert res["ledger"]["recv_dropped"].sum() > 0
+    shapes = set()
+    for r in range(R):
+        pool_ids = np.stack([res["dispatch"][s]["pool_ids"][r] for s in range(R)])
+        pool_rows = np.stack([res["dispatch"][s]["pool_rows"][r] for s in range(R)])
+        for experts in O.wave_experts(X, sh.waves):
+            got = O.wave_buffer(pool_rows, res["recv"][r], experts, rcap)
+            want = _brute_wave_buffer(pool_ids, pool_rows, r, X, experts, rcap)
+            assert np.array_equal(got, want)
+            shapes.add(got.shape)
+    assert len(shapes) == 1, "every wave buffer has the same shape"
+
+
 def test_expert_permutation_invariance_without_drops():
     from dataclasses import replace
     sh = replace(configs.get("mini_f32"), send_num=100000, recv_num=100000)
@@ -391,11 +504,16 @@ def test_ledger_invariants(name):
         rv = res["recv"][r]
         assert np.all(rv["count"] <= rcap)
         assert np.array_equal(rv["arrivals"], rv["count"] + rv["recv_dropped"])
-        # every returned row addressed by a kept assignment is a kept receive row or a zero row
-    if name != "cfg1":
-        assert led["send_dropped"].sum() > 0 and led["recv_dropped"].sum() > 0
-    else:
-        assert led["send_dropped"].sum() > 0 and led["recv_dropped"].sum() > 0
+        # a returned row is a zero row exactly where the row was dropped at receive
+        # or the slot is empty; every kept row carries an expert output (nonzero
+        # for these inputs: a zero output row would need every hidden value zero)
+        ret = res["ret"][r].reshape(-1, sh.latent)
+        zero = ~np.any(ret != 0, axis=1)
+        rank, expert = rv["row_rank"].reshape(-1), rv["row_expert"].reshape(-1)
+        kept_row = (expert >= 0) & (rank < rcap)
+        assert np.array_equal(zero, ~kept_row), f"rank {r}: zero returned rows != rows not kept"
+    # both caps bind in these workloads
+    assert led["send_dropped"].sum() > 0 and led["recv_dropped"].sum() > 0
 
 
 def test_one_rank_layer_matches_all_rank_emulation():
@@ -500,3 +618,36 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(O, "combine", unweighted)
     res = O.layer_all_ranks(sh, inp)
     assert not np.allclose(res["out"][0]["out_exact"][0], ref, rtol=1e-6)
+    monkeypatch.setattr(O, "combine", orig_c)
+
+    # 5. rows past recv_cap return expert outputs instead of zero rows
+    orig_r = O.expert_returns
+
+    def leaky(pool_rows, recv, w13, w2, hidden, act):
+        X = len(recv["count"])
+        je, rk = recv["row_expert"].reshape(-1), recv["row_rank"].reshape(-1)
+        row_src = np.full((X, max(int(recv["arrivals"].max()), 1)), -1, dtype=np.int64)
+        for j in range(X):
+            pos = np.flatnonzero(je == j)
+            row_src[j, rk[pos]] = pos
+        return orig_r(pool_rows, dict(recv, count=recv["arrivals"], row_src=row_src), w13, w2, hidden, act)
+
+    monkeypatch.setattr(O, "expert_returns", leaky)
+    with pytest.raises(AssertionError):
+        test_receive_dropped_assignment_contributes_nothing()
+    monkeypatch.setattr(O, "expert_returns", orig_r)
+
+    # 6. receive ranking slot-major instead of source-major
+    orig_s = O.recv_slots
+
+    def slot_major(pool_ids, my_rank, X, recv_cap):
+        r = orig_s(np.ascontiguousarray(pool_ids.T), my_rank, X, recv_cap)
+        n_src, cap = pool_ids.shape
+        pos = r["row_src"]
+        src_of = np.where(pos >= 0, (pos % n_src) * cap + pos // n_src, -1)
+        return dict(r, row_src=src_of, row_rank=r["row_rank"].T, row_expert=r["row_expert"].T)
+
+    monkeypatch.setattr(O, "recv_slots", slot_major)
+    with pytest.raises(AssertionError):
+        test_wave_buffer_by_enumeration()
+    monkeypatch.setattr(O, "recv_slots", orig_s)
