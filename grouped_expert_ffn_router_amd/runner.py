@@ -55,9 +55,12 @@ def pool_block_host(ids, rows, prow, act):
 class OneRankLayer:
     """One EP rank's layer.  ``inp`` is a workload.gen.generate() dict."""
 
-    def __init__(self, shape, inp, device="cuda", gather="fused"):
+    def __init__(self, shape, inp, device="cuda", gather="fused", keep_source_logits=False):
         self.shape, self.device = shape, device
         self.gather = gather
+        # keep_source_logits: the router logits each other rank computed at
+        # set-up, as host float32 arrays (source_logits[s]), for inspection
+        self.source_logits = {} if keep_source_logits else None
         r = int(inp["receiver"])
         self.rank = r
         self.dims = B.make_dims(shape, my_rank=r)
@@ -126,6 +129,8 @@ class OneRankLayer:
         B.pack_pools(d, self.z, self.idx, self.send_pools, self.scap * self.prow, self.slot_of, self.send_count,
                      self.ws)
         self.recv_pools[s].copy_(self.send_pools[self.rank])
+        if self.source_logits is not None:
+            self.source_logits[s] = self.logits.cpu().numpy()
         # rows source s wants to send here, before its send cap (the count a
         # dropless exchange would send ahead of the rows)
         self.source_demand[s] = B.drop_stats(d, self.ws, raise_on_bad_ids=False).send_demand[self.rank]

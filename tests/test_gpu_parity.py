@@ -550,6 +550,172 @@ def test_one_rank_full_size(runner, cfg):
     _say(f"[full-size] config {cfg}: bar ratio {ratio:.3g}, raw max|d|/rms {raw:.3g}")
 
 
+def _logit_bound(x, w, lg64):
+    """Largest difference an fp32 sum of the k products x_i*w_i (exact in
+    fp32 for bf16 operands) can have from the exact sum in ANY order,
+    (k-1)u/(1-(k-1)u) * sum|x_i w_i|, plus the rounding of the exact value to
+    fp32, u*|l|; u = 2^-24.  Per element, [T][E]."""
+    u = 2.0 ** -24
+    k = x.shape[1]
+    g = (k - 1) * u / (1 - (k - 1) * u)
+    return g * (np.abs(x) @ np.abs(w).T) + u * np.abs(lg64)
+
+
+def _full_size_shape(cfg):
+    if cfg == "4full":   # the Zipf-skewed routing through the whole layer: receive drops reach the experts
+        return replace(configs.get(4), name="cfg4_zipf_skew_full_layer", layer="full")
+    return configs.get(cfg)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [3, "4full", 6])
+def test_one_rank_full_size_bench_inputs(runner, cfg):
+    """One rank's layer at full size on the benchmark's own inputs (seed 0, x and
+    every weight drawn from N(0, .), not the exact grid), in the launch
+    configuration the benchmark times, compared with the oracle stage by stage
+    and element by element: each stage of the oracle takes the GPU's result of
+    the stage before where fp32 summation order could decide an integer (the
+    top-k selection runs on the GPU's fp32 logits: [P1 section 二], 8 of 384
+    by score) or where a row is moved between ranks (received pools).
+      * logits: every element within the any-order fp32 summation bound;
+      * topk_idx = the oracle's selection on the GPU's logits, exactly; weights
+        within 1e-5; z: every element;
+      * slot_of, send counts and drops, every pool id (own pools and the pools
+        all 63 other ranks send): exact; every payload row = the sender's z row
+        (exact for own rows, every element within the stored bar for others);
+      * receive ranks, counts and drops: exact;
+      * every returned row (the experts on the GPU's received rows): every
+        element; receive-dropped rows exactly zero;
+      * every element of the output against the oracle's chain from x (own
+        latent rows, own expert outputs, combine, up-projection, shared
+        experts), with the bar beyond the output's own rounding and the raw
+        max-abs error both reported; the raw error is asserted within
+        2e-2 RMS too."""
+    from concurrent.futures import ThreadPoolExecutor
+    sh = _full_size_shape(cfg)
+    scap, rcap = O.capacities(sh)
+    _say(f"[full-size bench inputs] {sh.name} seed=0 grid=False gather=fused")
+    inp = gen.generate(sh, seed=0, send_cap=scap)
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        drawn = dict(zip(range(sh.n_ranks), ex.map(inp["sources"], range(sh.n_ranks))))
+    inp["sources"] = drawn.__getitem__
+    lay = runner.OneRankLayer(sh, inp, gather="fused", keep_source_logits=True)
+    side = torch.cuda.Stream()
+    for _ in range(2):   # back to back, as timed
+        lay.run(side=side)
+    torch.cuda.synchronize()
+    rep = lay.drop_report()
+    r, R, X, L, act, k = inp["receiver"], sh.n_ranks, sh.local_experts, sh.latent, sh.act, sh.top_k
+    H = sh.expert_hidden
+    bias, brt = inp["bias"], inp["bias_row_tokens"]
+
+    # --- own routing
+    x64 = O.f64(inp["x"])
+    wr64 = O.f64(inp["w_router"])
+    gl = host(lay.logits)
+    ol = O.router_logits(inp["x"], inp["w_router"], bias, brt)
+    exact = x64 @ wr64.T
+    if bias is not None:
+        exact = exact + (np.asarray(bias, np.float64)[np.arange(sh.tokens) // brt] if brt else bias[0][None, :])
+    bound = _logit_bound(x64, wr64, exact)
+    dl = np.abs(gl.astype(np.float64) - exact)
+    assert np.all(dl <= bound), f"logits beyond the fp32 summation bound: worst {dl.max():.3g}"
+    _say(f"  logits: max |gpu - exact| {dl.max():.3g}, max |gpu - oracle fp32| "
+         f"{np.abs(gl - ol).max():.3g}, median bound {np.median(bound):.3g}")
+    del exact, bound, dl
+    idx, wt = O.select_topk(gl, k)
+    assert np.array_equal(host(lay.idx), idx), "topk_idx != the oracle's selection on the GPU's logits"
+    np.testing.assert_allclose(host(lay.w), wt, atol=1e-5, rtol=0, err_msg="topk_w")
+    nflip = int(np.sum(np.any(O.select_topk(ol, k)[0] != idx, axis=1)))
+    _say(f"  tokens whose top-{k} list differs between the GPU's and the oracle's own logits: {nflip}")
+    z_o = O.down_project(inp["x"], inp["w_down"], act)
+    gz = host(lay.z)
+    assert_stored_close(gz, z_o, act, "z (every element)")
+    sl = O.send_slots(idx, X, R, scap)
+    assert np.array_equal(host(lay.slot_of), sl["slot_of"]), "slot_of"
+    assert np.array_equal(host(lay.send_count), sl["send_count"]), "send_count"
+    assert rep["send_dropped"] == sl["send_dropped"] and rep["send_demand"] == list(sl["demand"])
+    pid, _ = O.pack_pools(idx, sl["slot_of"], R, scap)
+    ids, rows = _decode_pools(lay.send_pools, L, act)
+    assert np.array_equal(ids, pid), "own pool ids"
+    so = sl["slot_of"].reshape(-1)
+    tok = np.repeat(np.arange(sh.tokens), k)
+    ok = so >= 0
+    assert np.array_equal(rows.reshape(R * scap, L)[so[ok]], gz[tok[ok]]), "own pool payload != z rows"
+    del rows, ids
+    _say(f"  routing, z, slots and own pools checked ({int(ok.sum())} kept assignments)")
+
+    # --- the pools the other ranks send (their routing stage-wise on their GPU logits)
+    gids, grows = _decode_pools(lay.recv_pools, L, act)
+    rng = np.random.default_rng(1)
+    for s in range(R):
+        if s == r:
+            continue
+        xs = drawn[s]
+        g_ls = lay.source_logits[s]
+        sidx, _ = O.select_topk(g_ls, k)
+        ssl = O.send_slots(sidx, X, R, scap)
+        spid, _ = O.pack_pools(sidx, ssl["slot_of"], R, scap)
+        assert np.array_equal(gids[s], spid[r]), f"pool from source {s}: ids"
+        samp = rng.choice(sh.tokens, 64, replace=False)
+        xs64 = O.f64(xs[samp])
+        ex = xs64 @ wr64.T
+        if bias is not None:
+            ex = ex + (np.asarray(bias, np.float64)[samp // brt] if brt else bias[0][None, :])
+        assert np.all(np.abs(g_ls[samp] - ex) <= _logit_bound(xs64, wr64, ex)), f"source {s}: logits"
+        flat = ssl["slot_of"].reshape(-1)
+        mine = (flat >= r * scap) & (flat < (r + 1) * scap)
+        if mine.any():
+            slots = flat[mine] - r * scap
+            tokens = tok[mine]
+            zs = O.down_project(xs[tokens], inp["w_down"], act)
+            assert_stored_close(grows[s, slots], zs, act, f"payload rows from source {s}")
+    del drawn, inp["sources"]
+    lay.source_logits.clear()
+    _say("  pools from the other 63 ranks checked")
+
+    # --- receive side
+    rv = O.recv_slots(gids, r, X, rcap)
+    for w, experts in enumerate(O.wave_experts(X, sh.waves)):
+        assert np.array_equal(host(lay.wave_count[w]), rv["count"][experts]), f"wave {w}: counts"
+        assert np.array_equal(host(lay.row_src[w]), rv["row_src"][experts]), f"wave {w}: row_src"
+    assert rep["expert_arrivals"] == list(rv["arrivals"]) and rep["expert_kept"] == list(rv["count"])
+    assert rep["recv_dropped"] == rv["recv_dropped"].sum() and rep["recv_bad_ids"] == 0
+    if cfg == "4full":
+        assert rep["send_dropped"] > 0 and rep["recv_dropped"] > 0
+
+    # --- returned rows: the experts on the GPU's received rows
+    ret_o, defined = O.expert_returns(grows, rv, inp["w13"], inp["w2"], H, act)
+    gret = host(lay.ret_send)
+    kept_rows = defined & (rv["row_rank"] < rcap)
+    dropped_rows = defined & (rv["row_rank"] >= rcap)
+    assert not np.any(gret[dropped_rows]), "a receive-dropped row returned nonzero values"
+    assert_stored_close(gret[kept_rows], ret_o[kept_rows], act, "returned rows (every element)")
+    _say(f"  returned rows checked: {int(kept_rows.sum())} kept, {int(dropped_rows.sum())} dropped at receive")
+    del ret_o, gret, grows
+
+    # --- output: the oracle's chain from x for the own pool's rows
+    pool_self = np.zeros((scap, L))
+    own = so[ok] // scap == r
+    pool_self[so[ok][own] - r * scap] = z_o[tok[ok][own]]
+    ret_self = np.zeros((scap, L))
+    for j in range(X):
+        n = int(rv["count"][j])
+        q = rv["row_src"][j, :n]
+        q = q[q // scap == r] - r * scap
+        if q.size:
+            ret_self[q] = O.expert_ffn(pool_self[q], inp["w13"][j], inp["w2"][j], H, act)
+    ret_from_dest = O.f64(inp["foreign_ret"])
+    ret_from_dest[r] = ret_self
+    c = O.combine(ret_from_dest, sl["slot_of"], wt, scap, act)
+    del ret_from_dest
+    hs = O.shared_hidden(inp["x"], inp["ws13"], sh.shared_hidden, act)
+    _, out_exact = O.layer_output(c, hs, inp["w_up"], inp["ws2"], act)
+    ratio, raw = assert_bar(host(lay.out), out_exact, act, f"{sh.name} out (every element)")
+    _say(f"  out: bar ratio {ratio:.3g}, raw max|d|/rms {raw:.3g}")
+    assert raw <= 2e-2, f"raw max|d|/rms {raw:.3g} > 2e-2"
+
+
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_one_rank_ragged_full_size(runner, cfg):
     """The ragged dropless layer at one rank's real shape against the fixed-pool
