@@ -17,7 +17,8 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EDTYPE, MOE_ECAP, MOE_EHIP = 0, -1, -2, -3, 
 MOE_ACT_BF16, MOE_ACT_F32 = 0, 1
 MOE_MAX_RANKS, MOE_MAX_LOCAL = 1024, 64
 
-ENTRY_POINTS = ["moe_capacity", "moe_workspace_size", "moe_route", "moe_pack_pools", "moe_pack_ragged",
+ENTRY_POINTS = ["moe_capacity", "moe_workspace_size", "moe_route", "moe_pack_pools", "moe_pack_pools_noalloc",
+                "moe_pack_ragged",
                 "moe_recv_rank", "moe_recv_waves",
                 "moe_expert_gemm", "moe_shared_experts", "moe_combine", "moe_drop_stats", "moe_last_error", "moe_timing_enable",
                 "moe_timing_read"]
@@ -78,6 +79,7 @@ def lib():
     L.moe_workspace_size.argtypes = [DP, ctypes.POINTER(ctypes.c_size_t)]
     L.moe_route.argtypes = [DP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P]
     L.moe_pack_pools.argtypes = [DP, _P, _P, _P, _I64, _P, _P, _P, _P]
+    L.moe_pack_pools_noalloc.argtypes = [DP, _P, _P, _P, _I64, _P, _P, _P]
     L.moe_pack_ragged.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, _P]
     L.moe_recv_rank.argtypes = [DP, _P, _I64, _P, _P]
     L.moe_recv_waves.argtypes = [DP, _P, _I64, _I32, _P, _P, _P, _P, _P]
@@ -151,6 +153,11 @@ def pack_pools(dims, z, topk_idx, send_pools, dst_stride_bytes, slot_of, send_co
     _check(lib().moe_pack_pools(ctypes.byref(dims), _ptr(z), _ptr(topk_idx), _ptr(send_pools),
                                 int(dst_stride_bytes), _ptr(slot_of), _ptr(send_count), _ptr(ws),
                                 _stream(stream)))
+
+
+def pack_pools_noalloc(dims, z, topk_idx, send_pools, dst_stride_bytes, slot_of, send_count, stream=None):
+    _check(lib().moe_pack_pools_noalloc(ctypes.byref(dims), _ptr(z), _ptr(topk_idx), _ptr(send_pools),
+                                        int(dst_stride_bytes), _ptr(slot_of), _ptr(send_count), _stream(stream)))
 
 
 def pack_ragged(dims, z, topk_idx, send_rows, send_off, slot_of, send_count, ws, stream=None):

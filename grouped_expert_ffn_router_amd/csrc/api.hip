@@ -353,6 +353,90 @@ hipError_t up_and_shared_down(const Q& q, const void* ws2, const void* w_up, T* 
     return gemm_f32<false>("up_shared_down", a2, b2, e2, (int)q.D, (int)ldc, q.T, 1, st);
 }
 
+// ---------------------------------------------------------------- packing
+
+int check_pack_args(const Q& q, const void* z, const int32_t* topk_idx, const void* send_pools,
+                    int64_t dst_stride_bytes, const int32_t* slot_of, const int32_t* send_count) {
+  NEED_IF(q.scap > 0, send_pools, "send_pools"); NEED4(send_count, "send_count");
+  if (q.T > 0) { NEED(z, "z"); NEED4(topk_idx, "topk_idx"); NEED4(slot_of, "slot_of"); }
+  if (dst_stride_bytes % 16 || dst_stride_bytes < q.scap * q.prow)
+    return fail(MOE_EALIGN, "dst_stride_bytes must be a multiple of 16 and >= send_cap * pool_stride_bytes");
+  return MOE_OK;
+}
+
+// Rank, scan and pack with the given scratch: ctr (counters), s_cc / s_cb
+// ([R+1][nch] chunk counts and their scans) and s_lr ([T*k] ranks inside a
+// chunk).  Every scratch word a kernel reads was written earlier in the same
+// call, so the scratch needs no clearing.
+int pack_pools_run(const Q& q, const void* z, const int32_t* topk_idx, void* send_pools, int64_t dst_stride_bytes,
+                   int32_t* slot_of, int32_t* send_count, int32_t* ctr, int32_t* s_cc, int32_t* s_cb,
+                   int32_t* s_lr, int nch_s, hipStream_t st) {
+  LAUNCH("send_rank", st, launch_send_rank(topk_idx, (int)(q.T * q.k), (int)q.X, (int)q.E, (int)q.R, s_lr, s_cc, st),
+         "moe_pack_pools rank");
+  LAUNCH("send_scan", st, launch_send_scan(s_cc, nch_s, (int)q.R, (int)q.scap, s_cb, ctr, send_count, st),
+         "moe_pack_pools scan");
+  LAUNCH("pack", st, launch_pack(z, q.row_bytes, topk_idx, s_lr, s_cb, (int)q.T, (int)q.k, (int)q.X, (int)q.E,
+                                 (int)q.R, (int)q.scap, send_pools, dst_stride_bytes, q.prow, slot_of, send_count,
+                                 nullptr, st),
+         "moe_pack_pools pack");
+  return MOE_OK;
+}
+
+struct PackScratch {
+  size_t ctr, s_cc, s_cb, s_lr, total;
+  int nch_s;
+};
+
+// The pack path's part of the workspace layout, packed on its own.
+PackScratch pack_scratch_layout(const Q& q) {
+  PackScratch p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  p.nch_s = (int)ceil_div(q.T * q.k, SCAN_CHUNK);
+  p.ctr = take((Ctr::HEADER + 2 * q.R + 2 * q.X) * 4);
+  p.s_cc = take((size_t)(q.R + 1) * p.nch_s * 4);
+  p.s_cb = take((size_t)(q.R + 1) * p.nch_s * 4);
+  p.s_lr = take((size_t)q.T * q.k * 4);
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+// ------------------------------------------------------ allocation-free scratch
+// Scratch of moe_pack_pools_noalloc, for callers that cannot allocate device
+// memory.  Each GPU the library runs on holds its own copy of this array (at
+// its own address) until the process ends.  Host code never passes the
+// array's name to a kernel or a copy: in host code it is a stand-in, not a
+// device address.  It uses the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+char* g_scratch_addr[64] = {nullptr};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_base(char** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "moe_pack_pools_noalloc hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MOE_EINVAL, "moe_pack_pools_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "moe_pack_pools_noalloc hipGetSymbolAddress");
+    if (!p) return fail(MOE_EHIP, "moe_pack_pools_noalloc: no device address for the scratch array");
+    g_scratch_addr[dev] = (char*)p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 // =================================================================== C ABI
@@ -454,21 +538,30 @@ int moe_pack_pools(const moe_dims* dims, const void* z, const int32_t* topk_idx,
   Q q;
   int rc = derive(dims, &q);
   if (rc) return rc;
-  NEED_IF(q.scap > 0, send_pools, "send_pools"); NEED4(send_count, "send_count"); NEED(ws, "ws");
-  if (q.T > 0) { NEED(z, "z"); NEED4(topk_idx, "topk_idx"); NEED4(slot_of, "slot_of"); }
-  if (dst_stride_bytes % 16 || dst_stride_bytes < q.scap * q.prow)
-    return fail(MOE_EALIGN, "dst_stride_bytes must be a multiple of 16 and >= send_cap * pool_stride_bytes");
+  NEED(ws, "ws");
+  if ((rc = check_pack_args(q, z, topk_idx, send_pools, dst_stride_bytes, slot_of, send_count))) return rc;
   const WsLayout w = layout(q);
-  hipStream_t st = (hipStream_t)stream;
-  int32_t* ctr = at<int32_t>(ws, w.ctr);
-  LAUNCH("send_rank", st, launch_send_rank(topk_idx, (int)(q.T * q.k), (int)q.X, (int)q.E, (int)q.R, at<int32_t>(ws, w.s_lr),
-                           at<int32_t>(ws, w.s_cc), st), "moe_pack_pools rank");
-  LAUNCH("send_scan", st, launch_send_scan(at<int32_t>(ws, w.s_cc), w.nch_s, (int)q.R, (int)q.scap, at<int32_t>(ws, w.s_cb), ctr,
-                           send_count, st), "moe_pack_pools scan");
-  LAUNCH("pack", st, launch_pack(z, q.row_bytes, topk_idx, at<int32_t>(ws, w.s_lr), at<int32_t>(ws, w.s_cb), (int)q.T,
-                      (int)q.k, (int)q.X, (int)q.E, (int)q.R, (int)q.scap, send_pools, dst_stride_bytes, q.prow,
-                      slot_of, send_count, nullptr, st), "moe_pack_pools pack");
-  return MOE_OK;
+  return pack_pools_run(q, z, topk_idx, send_pools, dst_stride_bytes, slot_of, send_count, at<int32_t>(ws, w.ctr),
+                        at<int32_t>(ws, w.s_cc), at<int32_t>(ws, w.s_cb), at<int32_t>(ws, w.s_lr), w.nch_s,
+                        (hipStream_t)stream);
+}
+
+int moe_pack_pools_noalloc(const moe_dims* dims, const void* z, const int32_t* topk_idx, void* send_pools,
+                           int64_t dst_stride_bytes, int32_t* slot_of, int32_t* send_count, void* stream) {
+  Q q;
+  int rc = derive(dims, &q);
+  if (rc) return rc;
+  const PackScratch p = pack_scratch_layout(q);
+  if (p.total > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_EINVAL, "moe_pack_pools_noalloc: %lld tokens x %lld experts per token over %lld ranks need "
+                "%zu bytes of scratch, more than the %zu the library holds",
+                (long long)q.T, (long long)q.k, (long long)q.R, p.total, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  if ((rc = check_pack_args(q, z, topk_idx, send_pools, dst_stride_bytes, slot_of, send_count))) return rc;
+  char* base = nullptr;
+  if ((rc = scratch_base(&base))) return rc;
+  return pack_pools_run(q, z, topk_idx, send_pools, dst_stride_bytes, slot_of, send_count, (int32_t*)(base + p.ctr),
+                        (int32_t*)(base + p.s_cc), (int32_t*)(base + p.s_cb), (int32_t*)(base + p.s_lr), p.nch_s,
+                        (hipStream_t)stream);
 }
 
 int moe_pack_ragged(const moe_dims* dims, const void* z, const int32_t* topk_idx, void* send_rows,

@@ -134,6 +134,26 @@ int moe_pack_pools(const moe_dims* dims, const void* z, const int32_t* topk_idx,
                    void* send_pools, int64_t dst_stride_bytes, int32_t* slot_of,
                    int32_t* send_count, void* ws, void* stream);
 
+/* Allocation-free variant of moe_pack_pools, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * moe_pack_pools, without `ws`: the counters, chunk ranks and chunk scans
+ * live in a device array inside the library, MOE_NOALLOC_SCRATCH_BYTES
+ * large, which every GPU the library runs on holds until the process ends.
+ * Needs (16 + 2R + 2X) * 4 + 2 * (R + 1) * ceil(T*k / 1024) * 4 + T*k * 4
+ * bytes of it (each part rounded up to 256): at least 1,048,576
+ * assignments T*k for any R <= MOE_MAX_RANKS.  Larger inputs return
+ * MOE_EINVAL before anything is launched.  Nothing is allocated or freed
+ * and no allocating routine is called.  Every call on one GPU shares that
+ * GPU's scratch, whose contents the next call overwrites (nothing in it needs
+ * to start at zero): calls that overlap on one GPU (different streams or
+ * host threads without ordering between them) race.  The drop counters stay
+ * in the scratch; the kept rows per destination are send_count. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int moe_pack_pools_noalloc(const moe_dims* dims, const void* z, const int32_t* topk_idx,
+                           void* send_pools, int64_t dst_stride_bytes, int32_t* slot_of,
+                           int32_t* send_count, void* stream);
+
 /* Ragged packing for the dropless comparison (section 四 of the same page:
  * the first fallback is a dropless all-to-all whose row counts travel ahead
  * of the rows, so pools can be ragged).  No send cap applies: every valid

@@ -25,6 +25,14 @@ def test_library_exports_every_declared_entry_point():
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
+        # without argtypes ctypes would pass Python ints as 32-bit C ints,
+        # truncating pointers and stream handles
+        assert getattr(lib, n).argtypes is not None, f"{n}: no argtypes in the binding"
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe.h")).read(), flags=re.S)
+    for m in re.finditer(r"\b(moe_[a-z_]+)\s*\(([^)]*)\)\s*;", src):
+        args = m.group(2).strip()
+        n_args = 0 if args in ("", "void") else len(args.split(","))
+        assert len(getattr(lib, m.group(1)).argtypes) == n_args, f"{m.group(1)}: argtypes != the header's arguments"
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, "mini_bf16", "mini_bf16_skew", "mini_bf16_seg", "mini_f32"])
@@ -130,3 +138,18 @@ def test_header_compiles_as_c_and_the_host_entry_points_work_from_c(tmp_path):
     assert r.returncode == 0, r.stdout[-3000:]
     out = subprocess.run([str(exe)], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=120)
     assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout[-2000:]
+
+
+def test_pack_noalloc_refuses_inputs_over_its_scratch_before_any_launch():
+    """The allocation-free packing call holds its scratch in a fixed device
+    array; a batch that needs more is refused on the host (every pointer NULL
+    here, so nothing could run)."""
+    from dataclasses import replace
+    sh = replace(configs.get(2), tokens=600000)           # 4.8 M assignments
+    with pytest.raises(B.MoeError) as e:
+        B.pack_pools_noalloc(B.make_dims(sh), None, None, None, 0, None, None, stream=0)
+    assert e.value.code == B.MOE_EINVAL and "scratch" in str(e.value)
+    # within the scratch the usual argument checks apply, still before any launch
+    with pytest.raises(B.MoeError) as e:
+        B.pack_pools_noalloc(B.make_dims(configs.get(2)), 256, 256, 256, 100, 256, 256, stream=0)
+    assert e.value.code == B.MOE_EALIGN
