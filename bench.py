@@ -59,6 +59,12 @@ def parse():
     ap.add_argument("--streams", type=int, choices=[1, 2], default=2,
                     help="2: the shared experts and the odd waves run on a second stream, beside the routed "
                          "path and the even waves")
+    ap.add_argument("--live-waves", type=int, default=2,
+                    help="waves whose scratch (SwiGLU hidden rows, partial tiles) the workspace holds at once; "
+                         "2 (default): two waves overlap, one on each stream, as many as two streams can run; "
+                         "1: one wave live at a time, waves in order; 0: all waves")
+    ap.add_argument("--cpu-runs", type=int, default=0,
+                    help="timed runs of the CPU oracle (the median is reported); 0: 3, or 1 for 65,536 tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens per rank of the CPU-oracle sample (0: the whole workload)")
@@ -129,8 +135,9 @@ def algorithmic_work(sh, kept_rows_per_wave, send_kept, send_cap):
     }
 
 
-def cpu_baseline(cfg, seed, tokens):
-    """Time the CPU oracle on a bounded sample: the same layer at `tokens` tokens per rank."""
+def cpu_baseline(cfg, seed, tokens, runs):
+    """Time the CPU oracle on a bounded sample: the same layer at `tokens` tokens per rank
+    (median of `runs` runs)."""
     from oracle import moe_oracle as O
     from workload import configs, gen
     base = configs.get(cfg)
@@ -147,16 +154,53 @@ def cpu_baseline(cfg, seed, tokens):
             threads = int(info[0]["num_threads"])
     except Exception:
         pass
-    t0 = time.perf_counter()
-    O.layer_one_rank(sh, inp, with_floats=True)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(max(runs, 1)):
+        t0 = time.perf_counter()
+        O.layer_one_rank(sh, inp, with_floats=True)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     what = "route + pack + receive" if sh.layer != "full" else "the full layer"
     scope = (f"the whole {base.name} workload" if tokens == base.tokens else
              f"the {base.name} recipe at {tokens} tokens per rank (send pools of {scap} rows)")
     return {"value": tokens * sh.top_k / dt, "unit": "assignments/s", "cores": threads, "kind": "oracle",
             "sample": f"{scope}: {what} of one rank in the float64 oracle (seed {seed}), input generation "
-                      f"excluded, one run of {dt:.1f} s",
+                      f"excluded, median of {len(times)} run(s): " + ", ".join(f"{t:.2f}" for t in times) + " s",
+            "runs_s": times,
             "host": {"cpu_model": _cpu_model(), "logical_cpus": os.cpu_count()}}
+
+
+def reference_rates(dev):
+    """What the device reaches outside this library, measured in the same run:
+    a plain device-to-device copy of 1 GiB (read + write bytes / time) and the
+    vendor bf16 GEMM (torch.matmul, hipBLASLt) on 8192^3 with N(0,1) operands."""
+    import torch
+    a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        b.copy_(a)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2 * a.numel() * 2 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    n = 8192
+    x = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    y = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        c = x @ y
+    e0.record()
+    for _ in range(10):
+        c = x @ y
+    e1.record()
+    torch.cuda.synchronize()
+    gemm = 2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del x, y, c
+    torch.cuda.empty_cache()
+    return {"device_copy_GBs": copy, "vendor_bf16_gemm_8192_TFLOPs": gemm}
 
 
 def _cpu_model():
@@ -367,7 +411,7 @@ def main():
     torch.cuda.set_device(0)
     scap, rcap, _ = binding.capacity(binding.make_dims(sh))
     inp = gen.generate(sh, seed=args.seed, send_cap=scap)
-    lay = runner.OneRankLayer(sh, inp, device=dev, gather=args.gather)
+    lay = runner.OneRankLayer(sh, inp, device=dev, gather=args.gather, live_waves=args.live_waves)
     del inp
     stream = torch.cuda.current_stream()
     full = sh.layer == "full"
@@ -376,14 +420,18 @@ def main():
     for _ in range(args.warmup):
         lay.run(stream, side)
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
+    # an event on the main stream before every step and after the last: a
+    # step's combine waits for its side-stream work, and the next step's
+    # side-stream work waits for that combine, so consecutive events bracket
+    # exactly one step
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.steps):
         lay.run(stream, side)
-    t1.record(stream)   # the last step's combine waited for its shared experts
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
 
     # per-kernel pass, all on one stream so that no two kernels share the
     # chip: every library launch bracketed by HIP events on its stream
@@ -401,6 +449,8 @@ def main():
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
+    rates = reference_rates(dev)
 
     rep = lay.drop_report(stream)
     T, k = sh.tokens, sh.top_k
@@ -424,28 +474,43 @@ def main():
     kind = work[dom][0] if dom in work else None
     out = {
         "metric": METRIC, "value": T * k / (ms * 1e-3), "unit": "assignments/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "step_ms": {"mean": ms, "median": float(np.median(step_ms)), "min": float(np.min(step_ms)),
+                    "max": float(np.max(step_ms))},
+        "kept_assignments_per_s": rep["send_kept"] / (ms * 1e-3),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if sh.act == "bf16" else "f32",
         "data": "synthetic (seeded; shapes of the pages' 4K-context expert layer)",
         "config": {"workload": sh.name, "tokens_per_rank": T, "d_model": sh.d_model, "latent": sh.latent,
                    "experts": sh.n_experts, "top_k": k, "ep_ranks": sh.n_ranks, "local_experts": sh.local_experts,
                    "waves": sh.waves, "expert_hidden": sh.expert_hidden, "shared_experts": sh.shared_experts,
                    "shared_hidden": sh.shared_hidden, "send_cap": scap, "recv_cap": rcap, "gather": args.gather,
+                   "live_waves": lay.live_waves, "streams": args.streams if full else 1,
                    "parallelism": "one EP rank of 64 (the other ranks' pools and returns are inputs)"},
     }
     if kind is not None:
         traffic = committed_traffic(dom, sh.name)
+        ceiling = rates["vendor_bf16_gemm_8192_TFLOPs"] if kind == "flop" else rates["device_copy_GBs"]
         out["roofline"] = {"bound": "mfma" if kind == "flop" else "hbm", "achieved": d["achieved"],
                            "peak": PEAK_MFMA_BF16_TFLOPS if kind == "flop" else PEAK_HBM_GBS, "unit": d["unit"],
                            "frac": d["frac"], "traffic": traffic, "kernel": dom, "avg_ms": d["avg_ms"],
-                           "work_per_launch": work[dom][1], "work_unit": kind}
+                           "work_per_launch": work[dom][1], "work_unit": kind,
+                           "measured_ceiling": ceiling, "frac_of_measured_ceiling": d["achieved"] / ceiling}
+    for name, ent in kernels.items():
+        if ent.get("unit") == "GB/s":
+            ent["frac_of_device_copy"] = ent["achieved"] / rates["device_copy_GBs"]
+        elif ent.get("unit") == "TFLOP/s":
+            ent["frac_of_vendor_gemm"] = ent["achieved"] / rates["vendor_bf16_gemm_8192_TFLOPs"]
     out["kernels"] = kernels
+    out["reference_rates"] = rates
+    out["memory"] = lay.memory()
     out["drops"] = {"send_dropped": rep["send_dropped"], "recv_dropped": rep["recv_dropped"],
                     "send_kept": rep["send_kept"], "recv_kept": rep["recv_kept"]}
     out["source_digest"] = source_digest()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.config, args.seed,
-                                           min(args.cpu_tokens, sh.tokens) if args.cpu_tokens else sh.tokens)
+        ctok = min(args.cpu_tokens, sh.tokens) if args.cpu_tokens else sh.tokens
+        runs = args.cpu_runs if args.cpu_runs else (1 if ctok >= 65536 else 3)
+        out["cpu_baseline"] = cpu_baseline(args.config, args.seed, ctok, runs)
     print(json.dumps(out))
 
 

@@ -117,7 +117,7 @@ class KernelTimer {  // scope guard around one launch
   } while (0)
 
 struct Q {  // validated, derived dimensions
-  int64_t T, D, L, E, k, R, X, W, WX, H, S, HS, esize, scap, rcap, prow, row_bytes, my_rank;
+  int64_t T, D, L, E, k, R, X, W, WX, LW, H, S, HS, esize, scap, rcap, prow, row_bytes, my_rank;
   bool bf16;
 };
 
@@ -141,6 +141,8 @@ int derive(const moe_dims* d, Q* q) {
   if (d->my_rank < 0 || d->my_rank >= d->n_ranks) return fail(MOE_EINVAL, "my_rank out of range");
   if (d->send_num <= 0 || d->send_den <= 0 || d->recv_num <= 0 || d->recv_den <= 0)
     return fail(MOE_EINVAL, "capacity factors must be positive rationals");
+  if (d->live_waves < 0 || d->live_waves > d->waves)
+    return fail(MOE_EINVAL, "live_waves %d out of range [0, waves = %d]", d->live_waves, d->waves);
   const bool bf16 = d->act_dtype == MOE_ACT_BF16;
   if (bf16) {
     if (d->d_model % 64 || d->latent % 64 || d->expert_hidden % 64 || d->shared_hidden % 64)
@@ -155,6 +157,7 @@ int derive(const moe_dims* d, Q* q) {
   }
   q->T = d->tokens; q->D = d->d_model; q->L = d->latent; q->E = d->n_experts; q->k = d->top_k;
   q->R = d->n_ranks; q->X = X; q->W = d->waves; q->WX = X / d->waves; q->H = d->expert_hidden;
+  q->LW = d->live_waves ? d->live_waves : d->waves;
   q->S = d->shared_experts; q->HS = d->shared_hidden; q->my_rank = d->my_rank; q->bf16 = bf16;
   q->esize = bf16 ? 2 : 4;
   const int64_t assign = q->T * q->k;
@@ -195,10 +198,10 @@ WsLayout layout(const Q& q) {
   w.r_rank = take((size_t)q.R * q.scap * 4);
   w.logits = take((size_t)q.T * q.E * 4);
   w.h_wave = (size_t)q.WX * q.rcap * q.H * q.esize;
-  w.h = take(w.h_wave * q.W);  // one SwiGLU hidden block per wave: waves may overlap
+  w.h = take(w.h_wave * q.LW);  // one SwiGLU hidden block per live wave: those waves may overlap
   w.cat = take((size_t)q.T * (q.L + q.S * q.HS) * q.esize);
   w.part_wave = q.bf16 ? (size_t)PART_SLOTS * PART_FLOATS * sizeof(float) : 0;  // tail-split partial tiles
-  w.part = take(w.part_wave * (q.W + 1));  // one block per wave, one for route / combine
+  w.part = take(w.part_wave * (q.LW + 1));  // one block per live wave, one for route / combine
   w.total = off;
   return w;
 }
@@ -657,10 +660,12 @@ int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf, co
   const WsLayout w = layout(q);
   hipStream_t st = (hipStream_t)stream;
   hipError_t r;
-  // the wave's own scratch (SwiGLU hidden rows, tail-split partials): waves may overlap
-  float* part = at<float>(ws, w.part + (size_t)(wave + 1) * w.part_wave);
+  // the scratch block of the wave (SwiGLU hidden rows, tail-split partials):
+  // waves in different blocks may overlap
+  const int64_t blk = wave % q.LW;
+  float* part = at<float>(ws, w.part + (size_t)(blk + 1) * w.part_wave);
   if (q.bf16) {
-    bf16_t* h = at<bf16_t>(ws, w.h + (size_t)wave * w.h_wave);
+    bf16_t* h = at<bf16_t>(ws, w.h + (size_t)blk * w.h_wave);
     if (wave_buf) {
       ARows<bf16_t> a{(const bf16_t*)wave_buf, q.L, q.rcap * q.L, wave_count, 0};
       r = expert_gemms<bf16_t>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, part, st);
@@ -669,7 +674,7 @@ int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf, co
       r = expert_gemms<bf16_t>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, part, st);
     }
   } else {
-    float* h = at<float>(ws, w.h + (size_t)wave * w.h_wave);
+    float* h = at<float>(ws, w.h + (size_t)blk * w.h_wave);
     if (wave_buf) {
       ARows<float> a{(const float*)wave_buf, q.L, q.rcap * q.L, wave_count, 0};
       r = expert_gemms<float>(q, a, wave, row_src, wave_count, w13, w2, ret_pools, ret_src_stride_bytes, h, part, st);

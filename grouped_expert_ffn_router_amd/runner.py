@@ -55,15 +55,17 @@ def pool_block_host(ids, rows, prow, act):
 class OneRankLayer:
     """One EP rank's layer.  ``inp`` is a workload.gen.generate() dict."""
 
-    def __init__(self, shape, inp, device="cuda", gather="fused", keep_source_logits=False):
+    def __init__(self, shape, inp, device="cuda", gather="fused", keep_source_logits=False, live_waves=0):
         self.shape, self.device = shape, device
         self.gather = gather
+        # waves whose scratch (hidden rows, partial tiles) the workspace holds at once
+        self.live_waves = live_waves if live_waves else shape.waves
         # keep_source_logits: the router logits each other rank computed at
         # set-up, as host float32 arrays (source_logits[s]), for inspection
         self.source_logits = {} if keep_source_logits else None
         r = int(inp["receiver"])
         self.rank = r
-        self.dims = B.make_dims(shape, my_rank=r)
+        self.dims = B.make_dims(shape, my_rank=r, live_waves=self.live_waves)
         self.scap, self.rcap, self.prow = B.capacity(self.dims)
         T, D, L, E, k, R = shape.tokens, shape.d_model, shape.latent, shape.n_experts, shape.top_k, shape.n_ranks
         X, W, H = shape.local_experts, shape.waves, shape.expert_hidden
@@ -171,11 +173,14 @@ class OneRankLayer:
 
     def run(self, stream=None, side=None):
         """One batch on `stream` (torch's current stream if None).  With `side`,
-        a second stream, the shared experts and the odd waves run there,
-        beside the routed path and the even waves: the shared experts start
-        once everything queued before on `stream` (the previous batch's
-        combine, which reads their output) is done, the odd waves once the
-        receive ranking is, and the combine waits for both."""
+        a second stream, the shared experts and the waves of odd scratch
+        blocks (wave w is in block w mod live_waves) run there, beside the
+        routed path and the other waves: the shared experts start once
+        everything queued before on `stream` (the previous batch's combine,
+        which reads their output) is done, the side waves once the receive
+        ranking is, and the combine waits for both.  A block's waves always
+        share a stream, so they run in order; with one live wave every wave
+        runs on `stream`."""
         main = stream if stream is not None else torch.cuda.current_stream()
         waves = self.shape.waves
         with torch.cuda.stream(main):
@@ -189,12 +194,12 @@ class OneRankLayer:
             self.dispatch(main)
             self.receive_rank(main)
             # a shared wave buffer ("buffer" gather) keeps the waves in order
-            two = side is not None and self.full and self.wave_buf is None
+            two = side is not None and self.full and self.wave_buf is None and self.live_waves > 1
             if two:
                 self._ev_ranked.record(main)
                 side.wait_event(self._ev_ranked)
             for w in range(waves):
-                st = side if two and w % 2 else main
+                st = side if two and (w % self.live_waves) % 2 else main
                 self.receive_wave(w, st)
                 if self.full:
                     self.expert_wave(w, st)
@@ -206,6 +211,19 @@ class OneRankLayer:
 
     def drop_report(self, stream=None):
         return B.drop_stats(self.dims, self.ws, stream, raise_on_bad_ids=False).as_dict()
+
+    def memory(self):
+        """Device bytes of one step's buffers.  The SwiGLU hidden rows of a wave
+        ([X/W][recv_cap][H] activations) are the part of the receive bank that
+        the waves keep small; the workspace holds live_waves such blocks."""
+        sh = self.shape
+        hidden_wave = (sh.local_experts // sh.waves) * self.rcap * sh.expert_hidden * self.esize if self.full else 0
+        exch = self.send_pools.numel() + self.recv_pools.numel()
+        ret = (self.ret_send.numel() + self.ret_recv.numel()) * self.esize if self.full else 0
+        return {"live_waves": self.live_waves, "hidden_rows_per_wave_bytes": hidden_wave,
+                "hidden_rows_live_bytes": hidden_wave * self.live_waves, "workspace_bytes": self.ws.numel(),
+                "wave_buffer_bytes": 0 if self.wave_buf is None else self.wave_buf.numel() * self.esize,
+                "exchange_pool_bytes": exch, "return_row_bytes": ret}
 
 
 class RaggedOneRankLayer(OneRankLayer):
@@ -225,6 +243,8 @@ class RaggedOneRankLayer(OneRankLayer):
         if "sources" not in inp:
             raise ValueError("the ragged layer needs a workload whose other ranks route their own tokens")
         self.shape, self.device, self.gather = shape, device, gather
+        self.live_waves = shape.waves
+        self.source_logits = None
         r = int(inp["receiver"])
         self.rank = r
         T, D, L, E, k, R = shape.tokens, shape.d_model, shape.latent, shape.n_experts, shape.top_k, shape.n_ranks

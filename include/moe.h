@@ -28,7 +28,8 @@
  *     between the calls of one layer.  Calls that share a workspace run in
  *     order on one stream, except: moe_shared_experts touches only its own
  *     region and may run beside the routed calls, and after moe_recv_rank the
- *     calls of different waves may run side by side.
+ *     calls of waves in different scratch blocks (dims.live_waves) may run
+ *     side by side.
  *   - Activations and weights are bf16 (act_dtype 0) or fp32 (act_dtype 1);
  *     accumulation is fp32; logits and routing weights are fp32.
  *   - Return 0 (MOE_OK) or a negative MOE_E* code; moe_last_error() returns a
@@ -74,6 +75,13 @@ typedef struct moe_dims {
   int32_t my_rank;   /* the rank whose experts moe_recv_waves / moe_expert_gemm serve */
   int32_t act_dtype; /* MOE_ACT_BF16 or MOE_ACT_F32 */
   int32_t send_num, send_den, recv_num, recv_den;
+  /* Waves whose scratch (SwiGLU hidden rows, GEMM partial tiles) the
+   * workspace holds at once, 1..W; 0 means W.  Wave w uses block w mod
+   * live_waves, so calls of two waves in one block must not overlap (run
+   * them in order on one stream).  1 keeps one wave's hidden rows live at a
+   * time (section 二: the waves exist so that only part of the receive bank
+   * is live); W lets every wave run beside the others. */
+  int32_t live_waves;
 } moe_dims;
 
 /* Drop ledger of one layer call on one rank; send side (this rank's tokens)
@@ -222,8 +230,9 @@ int moe_recv_waves(const moe_dims* dims, const void* recv_pools, int64_t src_str
  *   w2              [X][L][H] act
  *   ret_pools       return row of (s, slot) at ret_pools + s * ret_src_stride_bytes
  *                   + slot * L * sizeof(act)
- * Each wave has its own scratch in `ws`, so waves may overlap (see
- * moe_recv_waves); a wave_buf shared by two waves would not. */
+ * Wave w uses scratch block w mod live_waves of `ws` (dims.live_waves), so
+ * waves in different blocks may overlap (see moe_recv_waves); waves of one
+ * block, or sharing one wave_buf, must not. */
 int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf,
                     const void* recv_pools, int64_t src_stride_bytes, const int32_t* row_src,
                     const int32_t* wave_count, const void* w13, const void* w2,

@@ -15,8 +15,9 @@ static int fail(const char* what) {
 int main(void) {
   /* the 4K-context layer of one rank: 8192 tokens, 6144 -> 3072 latent, 384
      experts over 64 ranks, top-8, 3 waves, expert hidden 1536, 2 shared
-     experts of hidden 1536, factors 1.10 and 1.15 */
-  moe_dims d = {8192, 6144, 3072, 384, 8, 64, 3, 1536, 2, 1536, 0, MOE_ACT_BF16, 110, 100, 115, 100};
+     experts of hidden 1536, factors 1.10 and 1.15, the scratch of every wave
+     held at once (live_waves 0) */
+  moe_dims d = {8192, 6144, 3072, 384, 8, 64, 3, 1536, 2, 1536, 0, MOE_ACT_BF16, 110, 100, 115, 100, 0};
   int64_t send_cap = 0, recv_cap = 0, stride = 0;
   if (moe_capacity(&d, &send_cap, &recv_cap, &stride) != MOE_OK) return fail("moe_capacity");
   /* ceil(1.10 * 8192 * 8 / 64) = 1127; ceil(1.15 * 64 * 8192 * 8 / 384) = 12562;
@@ -24,6 +25,23 @@ int main(void) {
   if (send_cap != 1127 || recv_cap != 12562 || stride != 6272) return fail("capacities");
   size_t ws = 0;
   if (moe_workspace_size(&d, &ws) != MOE_OK || ws == 0 || ws % 256) return fail("moe_workspace_size");
+
+  /* one live wave: one block of SwiGLU hidden rows (2 x 12562 x 1536 bf16)
+     and one of partial tiles (256 tiles of 256 x 256 fp32) fewer per wave */
+  moe_dims one = d;
+  one.live_waves = 1;
+  size_t ws1 = 0;
+  if (moe_workspace_size(&one, &ws1) != MOE_OK) return fail("moe_workspace_size, one live wave");
+  if (ws - ws1 != 2 * ((size_t)2 * 12562 * 1536 * 2 + (size_t)256 * 256 * 256 * 4))
+    return fail("workspace of one live wave");
+  one.live_waves = 4;
+  if (moe_workspace_size(&one, &ws1) != MOE_EINVAL) return fail("live_waves > waves accepted");
+  /* the allocation-free packing refuses a batch over its scratch before any launch */
+  moe_dims big = d;
+  big.tokens = 600000;
+  if (moe_pack_pools_noalloc(&big, NULL, NULL, NULL, 0, NULL, NULL, NULL) != MOE_EINVAL ||
+      strstr(moe_last_error(), "scratch") == NULL)
+    return fail("oversized allocation-free packing accepted");
 
   moe_dims bad = d;
   bad.n_experts = 385; /* not a multiple of the rank count */

@@ -716,6 +716,39 @@ def test_one_rank_full_size_bench_inputs(runner, cfg):
     assert raw <= 2e-2, f"raw max|d|/rms {raw:.3g} > 2e-2"
 
 
+def test_live_waves_same_bits(runner):
+    """The workspace holding the scratch of 1, 2 or all 3 waves at once (one
+    wave live at a time, waves in order; or waves overlapping on two streams)
+    gives the same bits: the waves' results do not depend on their order."""
+    from concurrent.futures import ThreadPoolExecutor
+    sh = configs.get(3)
+    scap, _ = O.capacities(sh)
+    _say("[live waves] config 3, live_waves 3 / 2 / 1")
+    inp = gen.generate(sh, seed=4, send_cap=scap)
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        drawn = dict(zip(range(sh.n_ranks), ex.map(inp["sources"], range(sh.n_ranks))))
+    inp["sources"] = drawn.__getitem__
+    want = None
+    sizes = {}
+    for lw in (0, 2, 1):
+        lay = runner.OneRankLayer(sh, inp, gather="fused", live_waves=lw)
+        side = torch.cuda.Stream()
+        for _ in range(2):
+            lay.run(side=side)
+        torch.cuda.synchronize()
+        got = [host(t).view(np.uint8).copy() for t in (lay.out, lay.ret_send, lay.row_src, lay.wave_count)]
+        sizes[lay.live_waves] = lay.memory()
+        if want is None:
+            want = got
+        else:
+            for a, b, n in zip(got, want, ("out", "ret_send", "row_src", "wave_count")):
+                assert np.array_equal(a, b), f"live_waves {lay.live_waves}: {n} differs"
+        del lay
+        torch.cuda.empty_cache()
+    assert sizes[1]["hidden_rows_live_bytes"] * 3 == sizes[3]["hidden_rows_live_bytes"]
+    assert sizes[1]["workspace_bytes"] < sizes[2]["workspace_bytes"] < sizes[3]["workspace_bytes"]
+
+
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_one_rank_ragged_full_size(runner, cfg):
     """The ragged dropless layer at one rank's real shape against the fixed-pool
