@@ -197,3 +197,87 @@ def test_checker_catches_planted_hazards():
     assert _violations(loop_exit)
     loop_ok = loop_exit[:-1] + [";;#ASMSTART", "s_waitcnt lgkmcnt(0)", ";;#ASMEND", "v_or3_b32 v11, s19, v0, v244"]
     assert not _violations(loop_ok)
+
+
+# ------------------------------------------------ inline assembly allow-list
+
+# The only instructions the library may issue through inline assembly: LDS
+# fragment reads (whose registers the walk above tracks) and the waits and
+# barrier around them.  A vector-memory load written as inline assembly is
+# never allowed: the compiler treats its output register as written at once
+# and may hand it to another value (an address, say) while the load is still
+# in flight, which can fault the GPU.  Anything else is refused too: the
+# allow-list, not a list of bad forms, decides.
+ALLOWED_ASM = ("ds_read_b128", "s_waitcnt", "s_barrier")
+
+
+def _asm_blocks(asm):
+    """Instructions that came from inline assembly, with the function they sit in."""
+    out, in_asm, fn = [], False, None
+    for raw in asm.split("\n"):
+        t = raw.strip()
+        m = re.match(r"^(_Z\w+):", raw)
+        if m:
+            fn = m.group(1)
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        line = t.split(";")[0].strip()
+        if in_asm and line and not line.startswith("."):
+            out.append((fn, line))
+    return out
+
+
+def _asm_violations(asm):
+    bad = []
+    for fn, line in _asm_blocks(asm):
+        op = line.split()[0]
+        if not op.startswith(ALLOWED_ASM):
+            bad.append((fn, line))
+    return bad
+
+
+@pytest.fixture(scope="module")
+def kernels_asm(tmp_path_factory):
+    if not (os.path.exists(HIPCC) or shutil.which(HIPCC)):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa_k") / "kernels.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(CSRC, "kernels.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout[-3000:]
+    return out.read_text()
+
+
+def test_inline_assembly_is_only_lds_reads_waits_and_barriers(gemm_asm, kernels_asm):
+    for asm in (gemm_asm, kernels_asm):
+        bad = _asm_violations(asm)
+        assert not bad, f"{len(bad)} inline-assembly instructions outside the allow-list, first: {bad[:3]}"
+    assert _asm_blocks(gemm_asm), "the GEMM core's inline LDS reads were not found"
+
+
+def test_inline_assembly_check_catches_planted_loads():
+    planted = ["_Zfoo:", ";;#ASMSTART", "global_load_dwordx4 v[4:7], v[0:1], off", ";;#ASMEND"]
+    assert _asm_violations("\n".join(planted))
+    planted = ["_Zfoo:", ";;#ASMSTART", "buffer_load_dword v4, v0, s[0:3], 0 offen", ";;#ASMEND"]
+    assert _asm_violations("\n".join(planted))
+    planted = ["_Zfoo:", ";;#ASMSTART", "flat_load_dword v4, v[0:1]", ";;#ASMEND"]
+    assert _asm_violations("\n".join(planted))
+    ok = ["_Zfoo:", ";;#ASMSTART", "ds_read_b128 v[10:13], v2", ";;#ASMEND",
+          "global_load_dwordx4 v[4:7], v[0:1], off", ";;#ASMSTART", "s_waitcnt lgkmcnt(0)", ";;#ASMEND"]
+    assert not _asm_violations("\n".join(ok))
+
+
+def test_sources_hold_no_other_inline_assembly():
+    """Every asm statement in the library's sources is one of the allowed forms."""
+    for fname in sorted(os.listdir(CSRC)):
+        if not fname.endswith((".hip", ".h", ".cpp")):
+            continue
+        src = open(os.path.join(CSRC, fname)).read()
+        for m in re.finditer(r"\basm\s+volatile\s*\(\s*\"([^\"]*)\"", src):
+            op = m.group(1).split()[0]
+            assert op.startswith(ALLOWED_ASM), f"{fname}: inline assembly '{m.group(1)}' outside the allow-list"
