@@ -12,6 +12,8 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
+# built from the same sources with -DMOE_DEBUG (invariant flags, see use_debug)
+LIB_DEBUG_PATH = os.path.join(PKG, "libmoe_debug.so")
 
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EDTYPE, MOE_ECAP, MOE_EHIP = 0, -1, -2, -3, -4, -5
 MOE_ACT_BF16, MOE_ACT_F32 = 0, 1
@@ -60,20 +62,46 @@ class KernelTime(ctypes.Structure):
 
 
 _lib = None
+_loaded = {}
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 
 
 def lib():
-    """Load libmoe.so (raises if it has not been built)."""
+    """The library the calls below go to: libmoe.so unless use_debug() selected
+    its debug build (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+class use_debug:
+    """Context manager: calls made inside go to libmoe_debug.so, whose kernels
+    record invariant violations (a slot_of entry outside the return pools, a
+    rank inconsistent with its count) in the workspace; moe_drop_stats then
+    returns MOE_ECAP.  Results are otherwise those of libmoe.so."""
+
+    def __enter__(self):
+        global _lib
+        self._prev = lib()
+        _lib = _load(LIB_DEBUG_PATH)
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._prev
+        return False
+
+
+def _load(path):
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python -m grouped_expert_ffn_router_amd.build` (no fallback exists)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     DP = ctypes.POINTER(Dims)
     L.moe_capacity.argtypes = [DP, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
     L.moe_workspace_size.argtypes = [DP, ctypes.POINTER(ctypes.c_size_t)]
@@ -94,7 +122,7 @@ def lib():
     for n in ENTRY_POINTS:
         if n != "moe_last_error":
             getattr(L, n).restype = ctypes.c_int
-    _lib = L
+    _loaded[path] = L
     return L
 
 

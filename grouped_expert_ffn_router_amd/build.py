@@ -11,6 +11,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+# the same sources with -DMOE_DEBUG: kernels record invariant violations in
+# the workspace and moe_drop_stats reports them (MOE_ECAP); nothing traps
+LIB_DEBUG = os.path.join(PKG, "libmoe_debug.so")
 SOURCES = ["kernels.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,18 +34,25 @@ def _run(cmd):
 
 
 def build(verbose=False, extra_flags=()):
-    os.makedirs(BUILD, exist_ok=True)
-    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    """Build libmoe.so and its debug twin libmoe_debug.so (-DMOE_DEBUG)."""
+    variants = [(LIB, BUILD, ()), (LIB_DEBUG, os.path.join(BUILD, "debug"), ("-DMOE_DEBUG",))]
+    jobs = []
+    for _, bdir, flags in variants:
+        os.makedirs(bdir, exist_ok=True)
+        for src in SOURCES:
+            jobs.append((src, os.path.join(bdir, os.path.splitext(src)[0] + ".o"), flags))
 
-    def compile_one(src_obj):
-        src, obj = src_obj
-        return _run([HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    def compile_one(job):
+        src, obj, flags = job
+        return _run([HIPCC, *FLAGS, *flags, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        logs = list(ex.map(compile_one, zip(SOURCES, objs)))
-    tmp = LIB + ".tmp"
-    logs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-o", tmp, *objs]))
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        logs = list(ex.map(compile_one, jobs))
+    for lib, bdir, _ in variants:
+        objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        tmp = lib + ".tmp"
+        logs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-o", tmp, *objs]))
+        os.replace(tmp, lib)
     if verbose:
         for l in logs:
             if l.strip():

@@ -380,7 +380,7 @@ int pack_pools_run(const Q& q, const void* z, const int32_t* topk_idx, void* sen
          "moe_pack_pools scan");
   LAUNCH("pack", st, launch_pack(z, q.row_bytes, topk_idx, s_lr, s_cb, (int)q.T, (int)q.k, (int)q.X, (int)q.E,
                                  (int)q.R, (int)q.scap, send_pools, dst_stride_bytes, q.prow, slot_of, send_count,
-                                 nullptr, st),
+                                 nullptr, ctr, st),
          "moe_pack_pools pack");
   return MOE_OK;
 }
@@ -586,7 +586,7 @@ int moe_pack_ragged(const moe_dims* dims, const void* z, const int32_t* topk_idx
   LAUNCH("ragged_offsets", st, launch_ragged_offsets(send_count, (int)q.R, send_off, st), "moe_pack_ragged offsets");
   LAUNCH("pack", st, launch_pack(z, q.row_bytes, topk_idx, at<int32_t>(ws, w.s_lr), at<int32_t>(ws, w.s_cb), (int)q.T,
                       (int)q.k, (int)q.X, (int)q.E, (int)q.R, no_cap, send_rows, 0, q.prow, slot_of, send_count,
-                      send_off, st), "moe_pack_ragged pack");
+                      send_off, ctr, st), "moe_pack_ragged pack");
   return MOE_OK;
 }
 
@@ -607,7 +607,7 @@ int moe_recv_rank(const moe_dims* dims, const void* recv_pools, int64_t src_stri
                            (int)q.my_rank, at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cc),
                            st), "moe_recv_rank rank");
   LAUNCH("recv_scan", st, launch_recv_scan(at<int32_t>(ws, w.r_cc), w.nch_r, (int)q.X, (int)q.rcap, at<int32_t>(ws, w.r_cb),
-                           arrivals, kept, ctr + Ctr::RECV_BAD, st), "moe_recv_rank scan");
+                           arrivals, kept, ctr, st), "moe_recv_rank scan");
   LAUNCH("recv_final", st, launch_recv_final(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cb), n_rows,
                             (int)q.X, at<int32_t>(ws, w.r_rank), st), "moe_recv_rank final");
   return MOE_OK;
@@ -632,7 +632,7 @@ int moe_recv_waves(const moe_dims* dims, const void* recv_pools, int64_t src_str
   const int j0 = wave * (int)q.WX, nj = (int)q.WX, n_rows = (int)(q.R * q.scap);
   const int32_t* kept = ctr + Ctr::HEADER + 2 * q.R + q.X;
   LAUNCH("recv_place", st, launch_recv_place(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_rank), kept, n_rows, (int)q.rcap, j0,
-                            nj, wave_count, row_src, st), "moe_recv_waves place");
+                            nj, wave_count, row_src, ctr, st), "moe_recv_waves place");
   if (wave_buf)
     LAUNCH("wave_gather", st, launch_wave_gather(recv_pools, src_stride_bytes, q.prow, (int)q.scap, q.row_bytes, row_src, wave_count,
                                nj, (int)q.rcap, wave_buf, st), "moe_recv_waves gather");
@@ -719,8 +719,10 @@ int moe_combine(const moe_dims* dims, const void* ret_pools, int64_t ret_dst_str
   hipStream_t st = (hipStream_t)stream;
   void* cat = at<char>(ws, w.cat);
   const int64_t ldc = q.L + q.S * q.HS;
-  LAUNCH("combine", st, launch_combine(q.bf16 ? 0 : 1, ret_pools, ret_dst_stride_bytes, q.row_bytes, (int)q.scap, slot_of, topk_w,
-                         (int)q.T, (int)q.k, (int)q.L, cat, ldc, st), "moe_combine combine");
+  LAUNCH("combine", st, launch_combine(q.bf16 ? 0 : 1, ret_pools, ret_dst_stride_bytes, q.row_bytes, (int)q.scap,
+                                       (int)q.R, slot_of, topk_w, (int)q.T, (int)q.k, (int)q.L, cat, ldc,
+                                       at<int32_t>(ws, w.ctr), st),
+         "moe_combine combine");
   HIP_TRY(q.bf16 ? up_and_shared_down<bf16_t>(q, ws2, w_up, (bf16_t*)cat, out, at<float>(ws, w.part), st)
                  : up_and_shared_down<float>(q, ws2, w_up, (float*)cat, out, nullptr, st),
           "moe_combine gemm");
@@ -766,6 +768,13 @@ int moe_drop_stats(const moe_dims* dims, const void* ws, moe_drop_report* rep, v
   rep->recv_bad_ids = c[Ctr::RECV_BAD];
   if (rep->recv_bad_ids) return fail(MOE_ECAP, "%lld received rows carry an expert id of another rank",
                                      (long long)rep->recv_bad_ids);
+#ifdef MOE_DEBUG
+  if (c[Ctr::DBG_SEND]) return fail(MOE_ECAP, "debug check: a send rank below zero in the pack");
+  if (c[Ctr::DBG_COMBINE])
+    return fail(MOE_ECAP, "debug check: a slot_of entry outside [-1, n_ranks * send_cap) reached the combine "
+                "(the assignment was left out)");
+  if (c[Ctr::DBG_RECV]) return fail(MOE_ECAP, "debug check: a kept receive row ranked at or past its expert's count");
+#endif
   return MOE_OK;
 }
 

@@ -239,6 +239,9 @@ send_scan_kernel(const int32_t* __restrict__ chunk_count, int nch, int R, int ca
                  int32_t* __restrict__ ctr, int32_t* __restrict__ send_count_out) {
   const int d = blockIdx.x;
   const int total = column_scan(chunk_count + (int64_t)d * nch, chunk_base + (int64_t)d * nch, nch);
+#ifdef MOE_DEBUG
+  if (d == 0 && threadIdx.x == 0) ctr[Ctr::DBG_SEND] = ctr[Ctr::DBG_COMBINE] = 0;
+#endif
   if (threadIdx.x == 0) {
     if (d < R) {
       const int kept = min(total, cap);
@@ -288,7 +291,7 @@ pack_kernel(const char* __restrict__ z, int64_t row_bytes, const int32_t* __rest
             const int32_t* __restrict__ local_rank, const int32_t* __restrict__ chunk_base, int nch, int T, int k,
             int X, int E, int R, int cap, char* __restrict__ pools, int64_t dst_stride, int64_t prow,
             int32_t* __restrict__ slot_of, const int32_t* __restrict__ send_count,
-            const int32_t* __restrict__ ragged_off) {
+            const int32_t* __restrict__ ragged_off, int32_t* __restrict__ ctr) {
   const int t = blockIdx.x;
   const int tail = (int)((prow - row_bytes) >> 4);  // 16-byte chunks from the id to the end of the row
   if (t >= T) {
@@ -313,7 +316,10 @@ pack_kernel(const char* __restrict__ z, int64_t row_bytes, const int32_t* __rest
     if (e >= 0 && e < E) {
       const int d = e / X;
       const int r = chunk_base[(int64_t)d * nch + (int)(a / SCAN_CHUNK)] + local_rank[a];
-      if (ragged_off) {
+      MOE_DEBUG_FLAG(ctr, Ctr::DBG_SEND, r < 0);
+      if (r < 0) {
+        // unreachable: a rank is a count of earlier assignments
+      } else if (ragged_off) {
         slot = ragged_off[d] + r;
         o = (int64_t)slot * prow;
       } else if (r < cap) {
@@ -343,7 +349,7 @@ pack_kernel(const char* __restrict__ z, int64_t row_bytes, const int32_t* __rest
 hipError_t launch_pack(const void* z, int64_t row_bytes, const int32_t* idx, const int32_t* local_rank,
                        const int32_t* chunk_base, int T, int k, int X, int E, int R, int cap, void* pools,
                        int64_t dst_stride, int64_t prow, int32_t* slot_of, const int32_t* send_count,
-                       const int32_t* ragged_off, hipStream_t st) {
+                       const int32_t* ragged_off, int32_t* ctr, hipStream_t st) {
   const int nch = (T * k + SCAN_CHUNK - 1) / SCAN_CHUNK;
   const int64_t tail = (prow - row_bytes) >> 4;
   const int64_t fill_blocks = ragged_off ? 0 : ((int64_t)R * cap * tail + PACK_TPB - 1) / PACK_TPB;
@@ -351,7 +357,7 @@ hipError_t launch_pack(const void* z, int64_t row_bytes, const int32_t* idx, con
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(PACK_TPB), 0, st, (const char*)z, row_bytes, idx,
                      local_rank, chunk_base, nch, T, k, X, E, R, cap, (char*)pools, dst_stride, prow, slot_of,
-                     send_count, ragged_off);
+                     send_count, ragged_off, ctr);
   return hipGetLastError();
 }
 
@@ -386,7 +392,7 @@ hipError_t launch_recv_rank(const void* pools, int64_t src_stride, int64_t prow,
 
 __global__ void __launch_bounds__(256)
 recv_scan_kernel(const int32_t* __restrict__ chunk_count, int nch, int X, int rcap, int32_t* __restrict__ chunk_base,
-                 int32_t* __restrict__ arrivals, int32_t* __restrict__ kept, int32_t* __restrict__ bad) {
+                 int32_t* __restrict__ arrivals, int32_t* __restrict__ kept, int32_t* __restrict__ ctr) {
   const int j = blockIdx.x;
   const int total = column_scan(chunk_count + (int64_t)j * nch, chunk_base + (int64_t)j * nch, nch);
   if (threadIdx.x == 0) {
@@ -394,15 +400,18 @@ recv_scan_kernel(const int32_t* __restrict__ chunk_count, int nch, int X, int rc
       arrivals[j] = total;
       kept[j] = min(total, rcap);
     } else {
-      *bad = total;
+      ctr[Ctr::RECV_BAD] = total;
+#ifdef MOE_DEBUG
+      ctr[Ctr::DBG_RECV] = 0;
+#endif
     }
   }
 }
 
 hipError_t launch_recv_scan(const int32_t* chunk_count, int nch, int X, int rcap, int32_t* chunk_base,
-                            int32_t* arrivals, int32_t* kept, int32_t* bad, hipStream_t st) {
+                            int32_t* arrivals, int32_t* kept, int32_t* ctr, hipStream_t st) {
   hipLaunchKernelGGL(recv_scan_kernel, dim3(X + 1), dim3(256), 0, st, chunk_count, nch, X, rcap, chunk_base, arrivals,
-                     kept, bad);
+                     kept, ctr);
   return hipGetLastError();
 }
 
@@ -434,11 +443,15 @@ hipError_t launch_recv_final(const int32_t* row_j, const int32_t* row_lrank, con
 __global__ void __launch_bounds__(256)
 recv_place_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict__ row_rank,
                   const int32_t* __restrict__ kept, int n_rows, int rcap, int j0, int nj,
-                  int32_t* __restrict__ wave_count, int32_t* __restrict__ row_src) {
+                  int32_t* __restrict__ wave_count, int32_t* __restrict__ row_src, int32_t* __restrict__ ctr) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n_rows) {
     const int j = row_j[i], rank = row_rank[i];
-    if (j >= j0 && j < j0 + nj && rank >= 0 && rank < rcap) row_src[(int64_t)(j - j0) * rcap + rank] = i;
+    if (j >= j0 && j < j0 + nj && rank >= 0 && rank < rcap) {
+      // a kept row's rank lies below its expert's kept count
+      MOE_DEBUG_FLAG(ctr, Ctr::DBG_RECV, rank >= kept[j]);
+      row_src[(int64_t)(j - j0) * rcap + rank] = i;
+    }
   }
   if (i < nj * rcap) {
     const int jw = i / rcap, r = i - jw * rcap;
@@ -448,11 +461,12 @@ recv_place_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict__
 }
 
 hipError_t launch_recv_place(const int32_t* row_j, const int32_t* row_rank, const int32_t* kept, int n_rows,
-                             int rcap, int j0, int nj, int32_t* wave_count, int32_t* row_src, hipStream_t st) {
+                             int rcap, int j0, int nj, int32_t* wave_count, int32_t* row_src, int32_t* ctr,
+                             hipStream_t st) {
   const int n = max(max(n_rows, nj * rcap), nj);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(recv_place_kernel, dim3((n + 255) / 256), dim3(256), 0, st, row_j, row_rank, kept, n_rows, rcap,
-                     j0, nj, wave_count, row_src);
+                     j0, nj, wave_count, row_src, ctr);
   return hipGetLastError();
 }
 
@@ -568,14 +582,20 @@ constexpr int COMBINE_TPB = 384;  // one 8-element chunk per lane of a 3072-wide
 // One block per token: c = act(sum_i w_i * returned row i), i ascending, fp32.
 template <class T>
 __global__ void __launch_bounds__(COMBINE_TPB)
-combine_kernel(const char* __restrict__ ret, int64_t dst_stride, int64_t row_bytes, int cap,
+combine_kernel(const char* __restrict__ ret, int64_t dst_stride, int64_t row_bytes, int cap, int R,
                const int32_t* __restrict__ slot_of, const float* __restrict__ w, int k, int L,
-               T* __restrict__ c_out, int64_t ldc) {
+               T* __restrict__ c_out, int64_t ldc, int32_t* __restrict__ ctr) {
   const int t = blockIdx.x;
   __shared__ int64_t off[32];
   __shared__ float ww[32];
   if (threadIdx.x < k) {
-    const int s = slot_of[(int64_t)t * k + threadIdx.x];
+    int s = slot_of[(int64_t)t * k + threadIdx.x];
+#ifdef MOE_DEBUG
+    // a slot outside the return pools: reported, and the assignment left out
+    const bool bad = s < -1 || s >= R * cap;
+    MOE_DEBUG_FLAG(ctr, Ctr::DBG_COMBINE, bad);
+    if (bad) s = -1;
+#endif
     int64_t o = -1;
     if (s >= 0) {
       const int d = s / cap, sl = s - d * cap;
@@ -607,16 +627,16 @@ combine_kernel(const char* __restrict__ ret, int64_t dst_stride, int64_t row_byt
   }
 }
 
-hipError_t launch_combine(int act, const void* ret, int64_t dst_stride, int64_t row_bytes, int cap,
+hipError_t launch_combine(int act, const void* ret, int64_t dst_stride, int64_t row_bytes, int cap, int R,
                           const int32_t* slot_of, const float* w, int T, int k, int L, void* c_out, int64_t ldc,
-                          hipStream_t st) {
+                          int32_t* ctr, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (act == 0)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(COMBINE_TPB), 0, st, (const char*)ret, dst_stride,
-                       row_bytes, cap, slot_of, w, k, L, (bf16_t*)c_out, ldc);
+                       row_bytes, cap, R, slot_of, w, k, L, (bf16_t*)c_out, ldc, ctr);
   else
     hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(COMBINE_TPB), 0, st, (const char*)ret, dst_stride,
-                       row_bytes, cap, slot_of, w, k, L, (float*)c_out, ldc);
+                       row_bytes, cap, R, slot_of, w, k, L, (float*)c_out, ldc, ctr);
   return hipGetLastError();
 }
 

@@ -153,3 +153,43 @@ def test_pack_noalloc_refuses_inputs_over_its_scratch_before_any_launch():
     with pytest.raises(B.MoeError) as e:
         B.pack_pools_noalloc(B.make_dims(configs.get(2)), 256, 256, 256, 100, 256, 256, stream=0)
     assert e.value.code == B.MOE_EALIGN
+
+
+def test_c_client_and_host_code_under_address_sanitizer(tmp_path):
+    """The C client and the library's host code (argument checks, capacities,
+    workspace layout, error messages) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer on the host side only (-Xarch_host: the GPU
+    code is built as usual), run on the CPU: no report, same output."""
+    import shutil
+    import subprocess
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    clang = "/opt/rocm/llvm/bin/clang"
+    if not (os.path.exists(hipcc) and os.path.exists(clang)):
+        pytest.skip("hipcc / clang not available")
+    csrc = os.path.join(ROOT, "grouped_expert_ffn_router_amd", "csrc")
+    kernels_o = os.path.join(ROOT, "grouped_expert_ffn_router_amd", "_build", "kernels.o")
+    if not os.path.exists(kernels_o):
+        pytest.skip("build the library first")
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", csrc]
+    san = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_o = str(tmp_path / "api.o")
+    lib = str(tmp_path / "libmoe.so")
+
+    def run(cmd, **kw):
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, **kw)
+        assert r.returncode == 0, " ".join(cmd) + "\n" + r.stdout[-3000:]
+        return r.stdout
+
+    run([hipcc, "--offload-arch=gfx950", "-O1", "-g", "-fPIC", "-std=c++17", "-Xclang", "-target-feature",
+         "-Xclang", "-packed-fp32-ops", *san, *inc, "-c", os.path.join(csrc, "api.hip"), "-o", api_o])
+    run([hipcc, "--offload-arch=gfx950", "-shared", *san, "-o", lib, api_o, kernels_o])
+    exe = str(tmp_path / "abi_c_asan")
+    run([clang, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-g", "-fsanitize=address,undefined",
+         "-fno-omit-frame-pointer", "-I", os.path.join(ROOT, "include"),
+         os.path.join(ROOT, "tests", "native", "abi_c_check.c"), "-L", str(tmp_path), "-lmoe",
+         f"-Wl,-rpath,{tmp_path}", "-o", exe])
+    env = dict(os.environ, ASAN_OPTIONS="abort_on_error=0:halt_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    out = run([exe], env=env, timeout=120)
+    assert out.startswith("ok"), out[-2000:]
+    assert "ERROR: AddressSanitizer" not in out and "runtime error" not in out

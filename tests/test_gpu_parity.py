@@ -402,6 +402,59 @@ def test_all_logits_equal_degenerate_router(runner):
     assert np.all(host(lay.w) == np.float32(1.0 / sh.top_k))
 
 
+def test_debug_build_same_results_and_flags_bad_slots(runner):
+    """libmoe_debug.so (-DMOE_DEBUG): the same layer gives the same bits as
+    libmoe.so and reports no violation; a slot_of entry outside the return
+    pools (or below -1) handed to moe_combine is reported by moe_drop_stats
+    as MOE_ECAP and that assignment is left out, as if dropped (nothing traps
+    and nothing is read out of bounds)."""
+    from grouped_expert_ffn_router_amd import binding as B
+    sh = configs.get("mini_bf16")
+    _say("[debug build] mini_bf16")
+    inp = gen.generate(sh, seed=9, grid=True)
+    rel = runner.AllRanksLayer(sh, inp)
+    rel.run()
+    torch.cuda.synchronize()
+    with B.use_debug():
+        dbg = runner.AllRanksLayer(sh, inp)
+        dbg.run()
+        torch.cuda.synchronize()
+        for r in dbg.drop_reports():
+            assert r["recv_bad_ids"] == 0
+        for rk in range(sh.n_ranks):   # raises on any recorded violation
+            B.drop_stats(dbg.dims[rk], dbg.ws[rk])
+    for n in ("out", "ret", "slot_of", "row_src", "wave_count", "z", "logits"):
+        a, b = host(getattr(rel, n)), host(getattr(dbg, n))
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"debug build: {n} differs"
+    # corrupt two slots of rank 0's tokens 5 and 6
+    R, L, es = sh.n_ranks, sh.latent, 2
+    scap = rel.scap
+    bad = rel.slot_of[0].clone()
+    bad[5, 1] = R * scap + 3
+    bad[6, 0] = -7
+    dropped = rel.slot_of[0].clone()
+    dropped[5, 1] = -1
+    dropped[6, 0] = -1
+    ret_view = rel.ret[0, 0]
+    stride = R * scap * L * es
+    out_rel = torch.empty_like(rel.out[0])
+    B.combine(rel.dims[0], ret_view, stride, dropped, rel.w[0], rel.w_up, rel.ws2, out_rel, rel.ws[0])
+    torch.cuda.synchronize()
+    with B.use_debug():
+        out_dbg = torch.empty_like(dbg.out[0])
+        B.combine(dbg.dims[0], dbg.ret[0, 0], stride, bad, dbg.w[0], dbg.w_up, dbg.ws2, out_dbg, dbg.ws[0])
+        torch.cuda.synchronize()
+        with pytest.raises(B.MoeError) as e:
+            B.drop_stats(dbg.dims[0], dbg.ws[0])
+        assert e.value.code == B.MOE_ECAP and "slot_of" in str(e.value)
+        # the next layer on this workspace starts clean
+        dbg.run()
+        torch.cuda.synchronize()
+        B.drop_stats(dbg.dims[0], dbg.ws[0])
+    assert np.array_equal(host(out_dbg).view(np.uint8), host(out_rel).view(np.uint8)), \
+        "a bad slot is not left out like a dropped one"
+
+
 def test_deterministic_bitwise(runner):
     """Two runs give bit-identical results (no atomics, fixed reduction orders).
     Pool bytes are compared where the layer defines them: every id, and the
