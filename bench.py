@@ -269,7 +269,7 @@ def capacity_sweep(args):
             if drawn is None:
                 drawn = {s: inp["sources"](s) for s in range(sh.n_ranks)}
             inp["sources"] = drawn.__getitem__
-        lay = runner.OneRankLayer(sh, inp, device="cuda:0", gather=args.gather)
+        lay = runner.OneRankLayer(sh, inp, device="cuda:0", gather=args.gather, live_waves=args.live_waves)
         del inp
         full = sh.layer == "full"
         side = torch.cuda.Stream() if args.streams == 2 and full else None
@@ -330,7 +330,7 @@ def dropless(args):
         return inp
 
     def build(sh):
-        return runner.OneRankLayer(sh, inputs(sh), device="cuda:0", gather=args.gather)
+        return runner.OneRankLayer(sh, inputs(sh), device="cuda:0", gather=args.gather, live_waves=args.live_waves)
 
     def measure(lay, timed):
         side = torch.cuda.Stream() if args.streams == 2 and lay.full else None
@@ -374,11 +374,19 @@ def dropless(args):
     del lay
     torch.cuda.empty_cache()
     # ragged pools: laid end to end by destination, as long as the counts
-    lay = runner.RaggedOneRankLayer(base, inputs(sh), expert_rows, device="cuda:0", gather=args.gather)
+    lay = runner.RaggedOneRankLayer(base, inputs(sh), expert_rows, device="cuda:0", gather=args.gather,
+                                    live_waves=args.live_waves)
     ms_rag, rep = measure(lay, True)
     rag = {"rows_sent": int(lay.own_off[-1]), "rows_received": lay.n_recv, "recv_cap": lay.rcap,
-           "send_dropped": rep["send_dropped"], "recv_dropped": rep["recv_dropped"], "bytes": lay.footprint(),
-           "ms_per_step": ms_rag}
+           "wave_rows": lay.wave_rows, "send_dropped": rep["send_dropped"], "recv_dropped": rep["recv_dropped"],
+           "bytes": lay.footprint(), "workspace_bytes": lay.ws.numel(), "ms_per_step": ms_rag}
+    del lay
+    torch.cuda.empty_cache()
+    # the same ragged exchange with a bank of expert_rows hidden rows per expert
+    lay = runner.RaggedOneRankLayer(base, inputs(sh), expert_rows, device="cuda:0", gather=args.gather,
+                                    ragged_banks=False, live_waves=args.live_waves)
+    ms_rag_fixed, _ = measure(lay, True)
+    rag["fixed_banks"] = {"bytes": lay.footprint(), "workspace_bytes": lay.ws.numel(), "ms_per_step": ms_rag_fixed}
     print(json.dumps({"comparison": "dropless (capacities fitted to the exchanged counts; ragged pools) vs fixed "
                                     "factors", "workload": base.name, "fixed": fixed, "dropless": fit,
                       "ragged": rag,

@@ -36,7 +36,7 @@ class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "tokens", "d_model", "latent", "n_experts", "top_k", "n_ranks", "waves",
         "expert_hidden", "shared_experts", "shared_hidden", "my_rank", "act_dtype",
-        "send_num", "send_den", "recv_num", "recv_den", "live_waves")]
+        "send_num", "send_den", "recv_num", "recv_den", "live_waves", "wave_rows")]
 
 
 class DropReport(ctypes.Structure):
@@ -148,9 +148,10 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def make_dims(shape, my_rank=0, tokens=None, live_waves=0):
+def make_dims(shape, my_rank=0, tokens=None, live_waves=0, wave_rows=0):
     """moe_dims from a workload.configs.Shape-like object."""
-    return Dims(live_waves=live_waves, tokens=shape.tokens if tokens is None else tokens, d_model=shape.d_model,
+    return Dims(live_waves=live_waves, wave_rows=wave_rows, tokens=shape.tokens if tokens is None else tokens,
+                d_model=shape.d_model,
                 latent=shape.latent, n_experts=shape.n_experts, top_k=shape.top_k,
                 n_ranks=shape.n_ranks, waves=shape.waves, expert_hidden=shape.expert_hidden,
                 shared_experts=shape.shared_experts, shared_hidden=shape.shared_hidden,

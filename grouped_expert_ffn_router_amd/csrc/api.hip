@@ -117,7 +117,7 @@ class KernelTimer {  // scope guard around one launch
   } while (0)
 
 struct Q {  // validated, derived dimensions
-  int64_t T, D, L, E, k, R, X, W, WX, LW, H, S, HS, esize, scap, rcap, prow, row_bytes, my_rank;
+  int64_t T, D, L, E, k, R, X, W, WX, LW, WR, H, S, HS, esize, scap, rcap, prow, row_bytes, my_rank;
   bool bf16;
 };
 
@@ -143,6 +143,7 @@ int derive(const moe_dims* d, Q* q) {
     return fail(MOE_EINVAL, "capacity factors must be positive rationals");
   if (d->live_waves < 0 || d->live_waves > d->waves)
     return fail(MOE_EINVAL, "live_waves %d out of range [0, waves = %d]", d->live_waves, d->waves);
+  if (d->wave_rows < 0) return fail(MOE_EINVAL, "wave_rows %d < 0", d->wave_rows);
   const bool bf16 = d->act_dtype == MOE_ACT_BF16;
   if (bf16) {
     if (d->d_model % 64 || d->latent % 64 || d->expert_hidden % 64 || d->shared_hidden % 64)
@@ -158,6 +159,7 @@ int derive(const moe_dims* d, Q* q) {
   q->T = d->tokens; q->D = d->d_model; q->L = d->latent; q->E = d->n_experts; q->k = d->top_k;
   q->R = d->n_ranks; q->X = X; q->W = d->waves; q->WX = X / d->waves; q->H = d->expert_hidden;
   q->LW = d->live_waves ? d->live_waves : d->waves;
+  q->WR = d->wave_rows;
   q->S = d->shared_experts; q->HS = d->shared_hidden; q->my_rank = d->my_rank; q->bf16 = bf16;
   q->esize = bf16 ? 2 : 4;
   const int64_t assign = q->T * q->k;
@@ -197,7 +199,8 @@ WsLayout layout(const Q& q) {
   w.r_lr = take((size_t)q.R * q.scap * 4);
   w.r_rank = take((size_t)q.R * q.scap * 4);
   w.logits = take((size_t)q.T * q.E * 4);
-  w.h_wave = (size_t)q.WX * q.rcap * q.H * q.esize;
+  // hidden rows of a wave: a recv_cap block per expert, or one ragged bank
+  w.h_wave = (size_t)(q.WR > 0 ? q.WR : q.WX * q.rcap) * q.H * q.esize;
   w.h = take(w.h_wave * q.LW);  // one SwiGLU hidden block per live wave: those waves may overlap
   w.cat = take((size_t)q.T * (q.L + q.S * q.HS) * q.esize);
   w.part_wave = q.bf16 ? (size_t)PART_SLOTS * PART_FLOATS * sizeof(float) : 0;  // tail-split partial tiles
@@ -312,8 +315,8 @@ hipError_t expert_gemms(const Q& q, A a1, int wave, const int32_t* row_src, cons
                         hipStream_t st) {
   const int64_t x0 = (int64_t)wave * q.WX;
   BGateUp<T> b1{(const T*)w13 + x0 * 2 * q.H * q.L, q.L, 2 * q.H * q.L, (int)q.H, 0};
-  ESwiGLU<T> e1{h, q.H, q.rcap * q.H, 0};
-  ARows<T> a2{h, q.H, q.rcap * q.H, wave_count, 0};
+  ESwiGLU<T> e1{h, q.H, q.rcap * q.H, 0, wave_count, q.WR};
+  ARows<T> a2{h, q.H, q.rcap * q.H, wave_count, 0, q.WR};
   BRows<T> b2{(const T*)w2 + x0 * q.L * q.H, q.H, q.L * q.H};
   EScatter<T> e2{(char*)ret, ret_src_stride, q.row_bytes, (int)q.scap, row_src, q.rcap};
   hipError_t r;
@@ -632,7 +635,7 @@ int moe_recv_waves(const moe_dims* dims, const void* recv_pools, int64_t src_str
   const int j0 = wave * (int)q.WX, nj = (int)q.WX, n_rows = (int)(q.R * q.scap);
   const int32_t* kept = ctr + Ctr::HEADER + 2 * q.R + q.X;
   LAUNCH("recv_place", st, launch_recv_place(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_rank), kept, n_rows, (int)q.rcap, j0,
-                            nj, wave_count, row_src, ctr, st), "moe_recv_waves place");
+                            nj, q.WR, wave_count, row_src, ctr, st), "moe_recv_waves place");
   if (wave_buf)
     LAUNCH("wave_gather", st, launch_wave_gather(recv_pools, src_stride_bytes, q.prow, (int)q.scap, q.row_bytes, row_src, wave_count,
                                nj, (int)q.rcap, wave_buf, st), "moe_recv_waves gather");
@@ -768,6 +771,8 @@ int moe_drop_stats(const moe_dims* dims, const void* ws, moe_drop_report* rep, v
   rep->recv_bad_ids = c[Ctr::RECV_BAD];
   if (rep->recv_bad_ids) return fail(MOE_ECAP, "%lld received rows carry an expert id of another rank",
                                      (long long)rep->recv_bad_ids);
+  if (q.WR > 0 && c[Ctr::WAVE_OVER])
+    return fail(MOE_ECAP, "the kept rows of a wave exceed its hidden-row bank (wave_rows = %lld)", (long long)q.WR);
 #ifdef MOE_DEBUG
   if (c[Ctr::DBG_SEND]) return fail(MOE_ECAP, "debug check: a send rank below zero in the pack");
   if (c[Ctr::DBG_COMBINE])

@@ -30,14 +30,32 @@ namespace moe {
 // ------------------------------------------------------------ A operands
 // rows(g): rows of group g; row(g, m): pointer to element 0 of row m.
 
+// First row of group g in a bank whose groups are laid end to end: the rows
+// of the groups before it.
+__device__ __forceinline__ int64_t ragged_row0(const int32_t* counts, int g) {
+  int64_t r = 0;
+  for (int i = 0; i < g; ++i) r += counts[i];
+  return r;
+}
+
 template <class T>
 struct ARows {  // row m of group g at base + g*group_stride + m*lda
   const T* base;
   int64_t lda, group_stride;
   const int32_t* counts;  // device rows per group, or NULL: rows_const
   int rows_const;
+  // > 0: the groups' rows are laid end to end in a bank of ragged_rows rows
+  // (group g starts after the counts of the groups before it; group_stride
+  // unused); a row past the bank reads its last row
+  int64_t ragged_rows = 0;
   __device__ int rows(int g) const { return counts ? counts[g] : rows_const; }
-  __device__ const T* row(int g, int m) const { return base + g * group_stride + (int64_t)m * lda; }
+  __device__ const T* row(int g, int m) const {
+    if (ragged_rows > 0) {
+      const int64_t r = ragged_row0(counts, g) + m;
+      return base + (r < ragged_rows ? r : ragged_rows - 1) * lda;
+    }
+    return base + g * group_stride + (int64_t)m * lda;
+  }
 };
 
 template <class T>
@@ -210,12 +228,25 @@ struct ESwiGLU {  // hidden unit u of row m: act(silu(gate) * up)
   T* out;
   int64_t ldo, group_stride;
   int col0;
+  // > 0: groups laid end to end in a bank of ragged_rows rows, as ARows
+  // (rows per group from counts); a row past the bank is not stored
+  const int32_t* counts = nullptr;
+  int64_t ragged_rows = 0;
+  __device__ T* dest(int g, int m) const {
+    if (ragged_rows > 0) {
+      const int64_t r = ragged_row0(counts, g) + m;
+      return r < ragged_rows ? out + r * ldo + col0 : nullptr;
+    }
+    return out + g * group_stride + (int64_t)m * ldo + col0;
+  }
   __device__ void store2(int g, int m, int u, float gate, float up) const {
-    out[g * group_stride + (int64_t)m * ldo + col0 + u] = Act<T>::store(silu(gate) * up);
+    T* p = dest(g, m);
+    if (p) p[u] = Act<T>::store(silu(gate) * up);
   }
   struct Row { T* p; };
-  __device__ Row row(int g, int m) const { return {out + g * group_stride + (int64_t)m * ldo + col0}; }
+  __device__ Row row(int g, int m) const { return {dest(g, m)}; }
   __device__ void store4_pair(const Row& r, int u, const float* gate, const float* up) const {
+    if (!r.p) return;
     float h[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) h[i] = silu(gate[i]) * up[i];

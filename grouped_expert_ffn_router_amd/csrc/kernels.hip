@@ -401,6 +401,7 @@ recv_scan_kernel(const int32_t* __restrict__ chunk_count, int nch, int X, int rc
       kept[j] = min(total, rcap);
     } else {
       ctr[Ctr::RECV_BAD] = total;
+      ctr[Ctr::WAVE_OVER] = 0;
 #ifdef MOE_DEBUG
       ctr[Ctr::DBG_RECV] = 0;
 #endif
@@ -442,9 +443,14 @@ hipError_t launch_recv_final(const int32_t* row_j, const int32_t* row_lrank, con
 // Reads only what moe_recv_rank left, so waves may run side by side.
 __global__ void __launch_bounds__(256)
 recv_place_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict__ row_rank,
-                  const int32_t* __restrict__ kept, int n_rows, int rcap, int j0, int nj,
+                  const int32_t* __restrict__ kept, int n_rows, int rcap, int j0, int nj, int64_t wave_rows,
                   int32_t* __restrict__ wave_count, int32_t* __restrict__ row_src, int32_t* __restrict__ ctr) {
   const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i == 0 && wave_rows > 0) {  // the wave's kept rows must fit its hidden-row bank
+    int64_t n = 0;
+    for (int j = 0; j < nj; ++j) n += kept[j0 + j];
+    if (n > wave_rows) ctr[Ctr::WAVE_OVER] = 1;
+  }
   if (i < n_rows) {
     const int j = row_j[i], rank = row_rank[i];
     if (j >= j0 && j < j0 + nj && rank >= 0 && rank < rcap) {
@@ -461,12 +467,12 @@ recv_place_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict__
 }
 
 hipError_t launch_recv_place(const int32_t* row_j, const int32_t* row_rank, const int32_t* kept, int n_rows,
-                             int rcap, int j0, int nj, int32_t* wave_count, int32_t* row_src, int32_t* ctr,
-                             hipStream_t st) {
+                             int rcap, int j0, int nj, int64_t wave_rows, int32_t* wave_count, int32_t* row_src,
+                             int32_t* ctr, hipStream_t st) {
   const int n = max(max(n_rows, nj * rcap), nj);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(recv_place_kernel, dim3((n + 255) / 256), dim3(256), 0, st, row_j, row_rank, kept, n_rows, rcap,
-                     j0, nj, wave_count, row_src, ctr);
+                     j0, nj, wave_rows, wave_count, row_src, ctr);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ struct Ctr {
   static constexpr int SEND_DROPPED = 0;
   static constexpr int SEND_INVALID = 1;
   static constexpr int RECV_BAD = 2;
+  static constexpr int WAVE_OVER = 3;  // a wave's kept rows exceed its hidden-row bank (dims.wave_rows)
   // Debug builds (-DMOE_DEBUG) only: invariant flags.  A kernel that finds a
   // violation stores 1 in its word (every writer stores the same value, so no
   // atomics) and carries on without the offending access; nothing traps.
@@ -59,8 +60,8 @@ hipError_t launch_recv_scan(const int32_t* chunk_count, int nch, int X, int rcap
 hipError_t launch_recv_final(const int32_t* row_j, const int32_t* row_lrank, const int32_t* chunk_base, int n_rows,
                              int X, int32_t* row_rank, hipStream_t st);
 hipError_t launch_recv_place(const int32_t* row_j, const int32_t* row_rank, const int32_t* ctr_kept, int n_rows,
-                             int rcap, int j0, int nj, int32_t* wave_count, int32_t* row_src, int32_t* ctr,
-                             hipStream_t st);
+                             int rcap, int j0, int nj, int64_t wave_rows, int32_t* wave_count, int32_t* row_src,
+                             int32_t* ctr, hipStream_t st);
 hipError_t launch_wave_gather(const void* pools, int64_t src_stride, int64_t pool_row_stride, int cap,
                               int64_t row_bytes, const int32_t* row_src, const int32_t* wave_count, int nj,
                               int rcap, void* wave_buf, hipStream_t st);

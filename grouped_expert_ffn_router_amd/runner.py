@@ -217,7 +217,8 @@ class OneRankLayer:
         ([X/W][recv_cap][H] activations) are the part of the receive bank that
         the waves keep small; the workspace holds live_waves such blocks."""
         sh = self.shape
-        hidden_wave = (sh.local_experts // sh.waves) * self.rcap * sh.expert_hidden * self.esize if self.full else 0
+        rows = getattr(self, "wave_rows", 0) or (sh.local_experts // sh.waves) * self.rcap
+        hidden_wave = rows * sh.expert_hidden * self.esize if self.full else 0
         exch = self.send_pools.numel() + self.recv_pools.numel()
         ret = (self.ret_send.numel() + self.ret_recv.numel()) * self.esize if self.full else 0
         return {"live_waves": self.live_waves, "hidden_rows_per_wave_bytes": hidden_wave,
@@ -236,14 +237,19 @@ class RaggedOneRankLayer(OneRankLayer):
     every step, so the counts are too, and a step copies only the self
     segments of the two exchanges.  ``foreign_ret`` rows (the rows the other
     ranks return, [R][pool_rows][L]) are laid into this rank's ragged order
-    once.  ``expert_rows`` is the receive cap of every expert."""
+    once.  ``expert_rows`` is the receive cap of every expert.  With
+    ``ragged_banks`` each wave's hidden rows are laid end to end in one bank
+    sized to the largest number of rows any wave keeps (moe_dims.wave_rows),
+    from per-expert arrival counts taken at set-up (the counts a dropless
+    exchange would send ahead of the rows, split by expert); otherwise every
+    expert has a bank of expert_rows rows."""
 
-    def __init__(self, shape, inp, expert_rows, device="cuda", gather="fused"):
+    def __init__(self, shape, inp, expert_rows, device="cuda", gather="fused", ragged_banks=True, live_waves=2):
         from workload.configs import exact_fit
         if "sources" not in inp:
             raise ValueError("the ragged layer needs a workload whose other ranks route their own tokens")
         self.shape, self.device, self.gather = shape, device, gather
-        self.live_waves = shape.waves
+        self.live_waves = min(live_waves, shape.waves) if live_waves else shape.waves
         self.source_logits = None
         r = int(inp["receiver"])
         self.rank = r
@@ -283,23 +289,28 @@ class RaggedOneRankLayer(OneRankLayer):
             B.pack_ragged(setup_dims, self.z, self.idx, self.send_rows, self.send_off, self.slot_of,
                           self.send_count, ws_setup)
             off = self.send_off.cpu().numpy()
-            segs[s] = self.send_rows[int(off[r]):int(off[r + 1])].clone() if s != r else None
+            segs[s] = self.send_rows[int(off[r]):int(off[r + 1])].clone()
             if s == r:
                 self.own_off = off.astype(np.int64)
-        cnt = np.array([segs[s].shape[0] if s != r else self.own_off[r + 1] - self.own_off[r] for s in range(R)],
-                       dtype=np.int64)
+        cnt = np.array([segs[s].shape[0] for s in range(R)], dtype=np.int64)
         self.seg_off = np.concatenate([[0], np.cumsum(cnt)])
         self.n_recv = int(self.seg_off[-1])
         self.view_rows = max(-(-self.n_recv // R), 1)
-        self.recv_dims = B.make_dims(self._fit(self.view_rows), my_rank=r)
-        assert B.capacity(self.recv_dims)[:2] == (self.view_rows, self.rcap)
         self.scap = self.view_rows
         self.recv_pools = torch.empty((R * self.view_rows, self.prow), dtype=torch.uint8, device=dev)
         self.recv_pools.view(torch.int32)[self.n_recv:, (L * self.esize) // 4] = -1
-        for s in range(R):
-            if s != r and cnt[s]:
+        for s in range(R):   # the own segment too: a step copies the same rows again
+            if cnt[s]:
                 self.recv_pools[self.seg_off[s]:self.seg_off[s + 1]].copy_(segs[s])
         del segs, ws_setup
+        self.wave_rows = 0
+        if ragged_banks:
+            arr = receive_arrivals(shape, exact_fit(shape, self.view_rows, 1), r, self.recv_pools,
+                                   self.view_rows * self.prow, dev)
+            self.wave_rows = max(int(sum(arr[w * WX:(w + 1) * WX])) for w in range(W))
+        self.recv_dims = B.make_dims(self._fit(self.view_rows), my_rank=r, wave_rows=self.wave_rows,
+                                     live_waves=self.live_waves)
+        assert B.capacity(self.recv_dims)[:2] == (self.view_rows, self.rcap)
         # one workspace and one set of dims for the whole step (moe_pack_ragged
         # ignores the send cap, moe_combine reads the ragged return rows with
         # any cap)
@@ -368,6 +379,19 @@ class RaggedOneRankLayer(OneRankLayer):
         if self.full:
             n += (self.ret_send.numel() + self.ret_back.numel()) * self.esize
         return n
+
+
+def receive_arrivals(shape, fit_shape, rank, recv_pools, src_stride_bytes, device):
+    """Rows arriving at each local expert of ``rank`` from the pools in
+    ``recv_pools`` (a set-up pass of moe_recv_rank with a small workspace:
+    the ranking does not depend on the expert widths or the receive cap)."""
+    from dataclasses import replace
+    probe = replace(fit_shape, expert_hidden=64, shared_experts=0, shared_hidden=64)
+    d = B.make_dims(probe, my_rank=rank, live_waves=1, wave_rows=1)
+    ws = torch.zeros((B.workspace_size(d),), dtype=torch.uint8, device=device)
+    B.recv_rank(d, recv_pools, src_stride_bytes, ws)
+    rep = B.drop_stats(d, ws, raise_on_bad_ids=False)
+    return list(rep.expert_arrivals[:shape.local_experts])
 
 
 class AllRanksLayer:
@@ -462,10 +486,14 @@ class RaggedAllRanksLayer:
     -1 past the n received rows; the return rows go back into each sender's
     ragged order.  The two exchanges are device copies standing for the
     ragged all-to-all.  ``expert_rows`` sizes every expert's bank (the
-    receive cap)."""
+    receive cap).  ``wave_rows``: 0 keeps a bank of expert_rows hidden rows
+    per expert; None lays each wave's hidden rows end to end in one bank sized
+    to the rows that receiver's fullest wave keeps (per-expert arrival counts
+    at set-up, see RaggedOneRankLayer); a number forces that bank size."""
 
-    def __init__(self, shape, inp, expert_rows, device="cuda", gather="fused"):
+    def __init__(self, shape, inp, expert_rows, device="cuda", gather="fused", wave_rows=None):
         from workload.configs import exact_fit
+        self.wave_rows_arg = wave_rows
         self.shape, self.device, self.gather = shape, device, gather
         T, D, L, E, k, R = shape.tokens, shape.d_model, shape.latent, shape.n_experts, shape.top_k, shape.n_ranks
         X, W = shape.local_experts, shape.waves
@@ -528,8 +556,6 @@ class RaggedAllRanksLayer:
         for r in range(R):
             n = int(cnt[:, r].sum())
             view_rows = max(_ceil_div(n, R), 1)
-            d = B.make_dims(self._fit(view_rows), my_rank=r)
-            assert B.capacity(d)[:2] == (view_rows, self.rcap)
             seg = np.concatenate([[0], np.cumsum(cnt[:, r])])
             buf = torch.empty((R * view_rows, self.prow), dtype=torch.uint8, device=self.device)
             buf.view(torch.int32)[n:, id_col] = -1
@@ -537,6 +563,13 @@ class RaggedAllRanksLayer:
                 c = int(cnt[s, r])
                 if c:
                     buf[seg[s]:seg[s] + c].copy_(self.send_rows[s, off[s, r]:off[s, r] + c])
+            wave_rows = self.wave_rows_arg
+            if wave_rows is None:
+                arr = receive_arrivals(sh, self._fit(view_rows), r, buf, view_rows * self.prow, self.device)
+                WX = X // sh.waves
+                wave_rows = max(int(sum(arr[w * WX:(w + 1) * WX])) for w in range(sh.waves))
+            d = B.make_dims(self._fit(view_rows), my_rank=r, wave_rows=wave_rows)
+            assert B.capacity(d)[:2] == (view_rows, self.rcap)
             ws = torch.zeros((B.workspace_size(d),), dtype=torch.uint8, device=self.device)
             ret = torch.zeros((R * view_rows, L), dtype=self.out.dtype, device=self.device)
             pool_bytes = view_rows * self.prow

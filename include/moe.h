@@ -82,6 +82,16 @@ typedef struct moe_dims {
    * time (section 二: the waves exist so that only part of the receive bank
    * is live); W lets every wave run beside the others. */
   int32_t live_waves;
+  /* Hidden-row bank of a wave.  0: every local expert of the wave has its own
+   * block of recv_cap hidden rows (X/W * recv_cap rows per wave).  > 0: the
+   * hidden rows of the wave's experts are laid end to end (an expert's rows
+   * start after the kept rows of the wave's experts before it) in a bank of
+   * wave_rows rows; the caller guarantees that the kept rows of every wave
+   * fit, as a dropless exchange can from the counts it has exchanged
+   * ([P1] section 四: capacity costs memory).  A wave whose kept rows do not
+   * fit is reported by moe_drop_stats (MOE_ECAP); its rows past the bank are
+   * then not computed correctly (nothing is written outside the bank). */
+  int32_t wave_rows;
 } moe_dims;
 
 /* Drop ledger of one layer call on one rank; send side (this rank's tokens)

@@ -17,7 +17,7 @@ int main(void) {
      experts over 64 ranks, top-8, 3 waves, expert hidden 1536, 2 shared
      experts of hidden 1536, factors 1.10 and 1.15, the scratch of every wave
      held at once (live_waves 0) */
-  moe_dims d = {8192, 6144, 3072, 384, 8, 64, 3, 1536, 2, 1536, 0, MOE_ACT_BF16, 110, 100, 115, 100, 0};
+  moe_dims d = {8192, 6144, 3072, 384, 8, 64, 3, 1536, 2, 1536, 0, MOE_ACT_BF16, 110, 100, 115, 100, 0, 0};
   int64_t send_cap = 0, recv_cap = 0, stride = 0;
   if (moe_capacity(&d, &send_cap, &recv_cap, &stride) != MOE_OK) return fail("moe_capacity");
   /* ceil(1.10 * 8192 * 8 / 64) = 1127; ceil(1.15 * 64 * 8192 * 8 / 384) = 12562;
@@ -36,6 +36,14 @@ int main(void) {
     return fail("workspace of one live wave");
   one.live_waves = 4;
   if (moe_workspace_size(&one, &ws1) != MOE_EINVAL) return fail("live_waves > waves accepted");
+  /* a ragged hidden-row bank of 20000 rows per wave instead of 2 x 12562 */
+  moe_dims rag = d;
+  rag.wave_rows = 20000;
+  size_t ws2 = 0;
+  if (moe_workspace_size(&rag, &ws2) != MOE_OK) return fail("moe_workspace_size, ragged banks");
+  if (ws - ws2 != 3 * (size_t)(2 * 12562 - 20000) * 1536 * 2) return fail("workspace of ragged banks");
+  rag.wave_rows = -1;
+  if (moe_workspace_size(&rag, &ws2) != MOE_EINVAL) return fail("negative wave_rows accepted");
   /* the allocation-free packing refuses a batch over its scratch before any launch */
   moe_dims big = d;
   big.tokens = 600000;

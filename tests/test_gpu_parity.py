@@ -202,22 +202,27 @@ def _dropless_caps(base, inp):
             max(int(max(rv["arrivals"])) for rv in ref0["recv"]))
 
 
+@pytest.mark.parametrize("banks", ["ragged", "fixed"])
 @pytest.mark.parametrize("gather", ["fused", "buffer"])
 @pytest.mark.parametrize("name", ["cfg1", "mini_bf16_skew", "mini_bf16"])
-def test_all_ranks_ragged_dropless(runner, name, gather):
+def test_all_ranks_ragged_dropless(runner, name, gather, banks):
     """The ragged dropless exchange (pools laid end to end by destination, no send
     cap, receive buffers as long as what arrives): every integer result is the
     oracle's drop-free one moved to the ragged row order -- slot_of = offset of
     the destination + rank, row_src = offset of the source segment + slot -- and
-    the floats match the oracle's textbook layer within the bar."""
+    the floats match the oracle's textbook layer within the bar.  banks:
+    "ragged" lays each wave's hidden rows end to end in one bank as large as
+    the rows the receiver's fullest wave keeps; "fixed" gives every expert a
+    bank of the largest arrivals."""
     base = _shape(name)
     inp = gen.generate(base, seed=6, grid=True)
     pool_rows, expert_rows = _dropless_caps(base, inp)
     sh = configs.exact_fit(base, pool_rows, expert_rows)
-    _say(f"[ragged] {name} gather={gather} pool rows {pool_rows} expert rows {expert_rows}")
+    _say(f"[ragged] {name} gather={gather} banks={banks} pool rows {pool_rows} expert rows {expert_rows}")
     ref = O.layer_all_ranks(sh, inp)
     assert ref["ledger"]["kept"] == base.n_ranks * base.tokens * base.top_k
-    lay = runner.RaggedAllRanksLayer(base, inp, expert_rows, gather=gather)
+    lay = runner.RaggedAllRanksLayer(base, inp, expert_rows, gather=gather,
+                                     wave_rows=None if banks == "ragged" else 0)
     lay.run()
     torch.cuda.synchronize()
     R, L, act, k = base.n_ranks, base.latent, base.act, base.top_k
@@ -272,6 +277,37 @@ def test_all_ranks_ragged_dropless(runner, name, gather):
         assert_stored_close(np.concatenate(got_rows), np.concatenate(want_rows), act, f"rank {r} returned rows")
     for s in range(R):
         assert_bar(host(lay.out[s]), ref["out"][s]["out_exact"], act, f"src {s} out")
+    if banks == "ragged":
+        X, W = base.local_experts, base.waves
+        for r in range(R):
+            arr = ref["recv"][r]["arrivals"]
+            want = max(int(arr[w * (X // W):(w + 1) * (X // W)].sum()) for w in range(W))
+            assert lay.recv_dims[r].wave_rows == want, f"rank {r}: hidden-row bank"
+
+
+def test_ragged_bank_overflow_is_reported(runner):
+    """A hidden-row bank smaller than a wave's kept rows (a caller's mistake):
+    moe_drop_stats reports MOE_ECAP, and nothing is written outside the bank
+    (the rows past it are not computed correctly; the layer still ends
+    normally)."""
+    from grouped_expert_ffn_router_amd import binding as B
+    base = _shape("mini_bf16")
+    inp = gen.generate(base, seed=6, grid=True)
+    _, expert_rows = _dropless_caps(base, inp)
+    _say(f"[ragged bank overflow] mini_bf16 wave_rows 7 (expert rows {expert_rows})")
+    lay = runner.RaggedAllRanksLayer(base, inp, expert_rows, wave_rows=7)
+    lay.run()
+    torch.cuda.synchronize()
+    for r in range(base.n_ranks):
+        with pytest.raises(B.MoeError) as e:
+            B.drop_stats(lay.recv_dims[r], lay.ws_recv[r])
+        assert e.value.code == B.MOE_ECAP and "wave_rows" in str(e.value)
+    # a layer whose banks fit reports nothing on the same inputs
+    ok = runner.RaggedAllRanksLayer(base, inp, expert_rows)
+    ok.run()
+    torch.cuda.synchronize()
+    for r in range(base.n_ranks):
+        B.drop_stats(ok.recv_dims[r], ok.ws_recv[r])
 
 
 @pytest.mark.parametrize("tokens", [0, 1, 65])
@@ -842,7 +878,12 @@ def test_one_rank_ragged_full_size(runner, cfg):
     torch.cuda.synchronize()
     rrep = rag.drop_report()
     _say(f"[ragged full-size] config {cfg}: pool rows {pool_rows}, expert rows {expert_rows}, "
-         f"received {rag.n_recv} rows")
+         f"received {rag.n_recv} rows, hidden-row bank of {rag.wave_rows} rows per wave")
+    X, W = sh.local_experts, sh.waves
+    arr = rrep["expert_arrivals"]
+    assert rag.wave_rows == max(sum(arr[w * (X // W):(w + 1) * (X // W)]) for w in range(W))
+    from grouped_expert_ffn_router_amd import binding as B
+    B.drop_stats(rag.dims, rag.ws)   # the banks fit: no report
     assert frep["send_dropped"] == 0 and frep["recv_dropped"] == 0
     assert rrep["send_dropped"] == 0 and rrep["recv_dropped"] == 0
     assert rrep["send_demand"] == frep["send_demand"] and rrep["expert_arrivals"] == frep["expert_arrivals"]
