@@ -657,7 +657,7 @@ def _full_size_shape(cfg):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg", [3, "4full", 6])
+@pytest.mark.parametrize("cfg", [3, "4full", 6, 5])
 def test_one_rank_full_size_bench_inputs(runner, cfg):
     """One rank's layer at full size on the benchmark's own inputs (seed 0, x and
     every weight drawn from N(0, .), not the exact grid), in the launch
@@ -679,16 +679,24 @@ def test_one_rank_full_size_bench_inputs(runner, cfg):
         latent rows, own expert outputs, combine, up-projection, shared
         experts), with the bar beyond the output's own rounding and the raw
         max-abs error both reported; the raw error is asserted within
-        2e-2 RMS too."""
+        2e-2 RMS too.
+    Config 5 (65,536 tokens; the other ranks' pools are drawn inputs, not
+    routed): the received pools must equal those inputs byte for byte, and
+    the returned rows are checked element by element for every row of the
+    rank's own pool plus 2,048 sampled rows of each expert (its 500,000 rows
+    would take the float64 oracle minutes); everything else as above."""
     from concurrent.futures import ThreadPoolExecutor
     sh = _full_size_shape(cfg)
     scap, rcap = O.capacities(sh)
     _say(f"[full-size bench inputs] {sh.name} seed=0 grid=False gather=fused")
     inp = gen.generate(sh, seed=0, send_cap=scap)
-    with ThreadPoolExecutor(max_workers=16) as ex:
-        drawn = dict(zip(range(sh.n_ranks), ex.map(inp["sources"], range(sh.n_ranks))))
-    inp["sources"] = drawn.__getitem__
-    lay = runner.OneRankLayer(sh, inp, gather="fused", keep_source_logits=True)
+    routed = "sources" in inp
+    drawn = None
+    if routed:
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            drawn = dict(zip(range(sh.n_ranks), ex.map(inp["sources"], range(sh.n_ranks))))
+        inp["sources"] = drawn.__getitem__
+    lay = runner.OneRankLayer(sh, inp, gather="fused", keep_source_logits=routed)
     side = torch.cuda.Stream()
     for _ in range(2):   # back to back, as timed
         lay.run(side=side)
@@ -735,11 +743,17 @@ def test_one_rank_full_size_bench_inputs(runner, cfg):
     _say(f"  routing, z, slots and own pools checked ({int(ok.sum())} kept assignments)")
 
     # --- the pools the other ranks send (their routing stage-wise on their GPU logits)
-    gids, grows = _decode_pools(lay.recv_pools, L, act)
     rng = np.random.default_rng(1)
-    for s in range(R):
-        if s == r:
-            continue
+    gids = _decode_ids(lay.recv_pools, L, act)
+    others = [s for s in range(R) if s != r]
+    if not routed:
+        # drawn inputs: received as given, byte for byte
+        assert np.array_equal(gids[others], inp["foreign_ids"][others]), "received pool ids"
+        got = lay.recv_pools.view(torch.int16)[:, :, :L].cpu().numpy().view(np.uint16)
+        filled = inp["foreign_ids"][others] >= 0
+        assert np.array_equal(got[others][filled], inp["foreign_rows"][others][filled]), "received payload rows"
+        del got
+    for s in (others if routed else []):
         xs = drawn[s]
         g_ls = lay.source_logits[s]
         sidx, _ = O.select_topk(g_ls, k)
@@ -758,9 +772,12 @@ def test_one_rank_full_size_bench_inputs(runner, cfg):
             slots = flat[mine] - r * scap
             tokens = tok[mine]
             zs = O.down_project(xs[tokens], inp["w_down"], act)
-            assert_stored_close(grows[s, slots], zs, act, f"payload rows from source {s}")
-    del drawn, inp["sources"]
-    lay.source_logits.clear()
+            _, prow_vals = _decode_pools(lay.recv_pools[s][torch.as_tensor(slots, device=lay.recv_pools.device)],
+                                         L, act)
+            assert_stored_close(prow_vals, zs, act, f"payload rows from source {s}")
+    if routed:
+        del drawn, inp["sources"]
+        lay.source_logits.clear()
     _say("  pools from the other 63 ranks checked")
 
     # --- receive side
@@ -774,14 +791,38 @@ def test_one_rank_full_size_bench_inputs(runner, cfg):
         assert rep["send_dropped"] > 0 and rep["recv_dropped"] > 0
 
     # --- returned rows: the experts on the GPU's received rows
-    ret_o, defined = O.expert_returns(grows, rv, inp["w13"], inp["w2"], H, act)
-    gret = host(lay.ret_send)
+    defined = rv["row_expert"] >= 0
     kept_rows = defined & (rv["row_rank"] < rcap)
     dropped_rows = defined & (rv["row_rank"] >= rcap)
-    assert not np.any(gret[dropped_rows]), "a receive-dropped row returned nonzero values"
-    assert_stored_close(gret[kept_rows], ret_o[kept_rows], act, "returned rows (every element)")
-    _say(f"  returned rows checked: {int(kept_rows.sum())} kept, {int(dropped_rows.sum())} dropped at receive")
-    del ret_o, gret, grows
+    flat_ret = lay.ret_send.view(R * scap, L)
+    drop_idx = np.flatnonzero(dropped_rows.reshape(-1))
+    if drop_idx.size:
+        assert not torch.any(flat_ret[torch.as_tensor(drop_idx, device=flat_ret.device)] != 0).item(), \
+            "a receive-dropped row returned nonzero values"
+    pick = []          # (expert, pool rows) to compare
+    for j in range(X):
+        q = rv["row_src"][j, :int(rv["count"][j])].astype(np.int64)
+        if routed:
+            pick.append((j, q))
+        else:
+            own_q = q[q // scap == r]
+            samp = rng.choice(q, min(q.size, 2048), replace=False) if q.size else q
+            pick.append((j, np.unique(np.concatenate([own_q, samp]))))
+    flat_pool = lay.recv_pools.view(R * scap, -1)
+    n_checked = 0
+    got_all, want_all = [], []
+    for j, q in pick:
+        if not q.size:
+            continue
+        qd = torch.as_tensor(q, device=flat_pool.device)
+        _, rows_j = _decode_pools(flat_pool[qd], L, act)
+        want_all.append(O.expert_ffn(rows_j, inp["w13"][j], inp["w2"][j], H, act))
+        got_all.append(host(flat_ret[qd]))
+        n_checked += q.size
+    assert_stored_close(np.concatenate(got_all), np.concatenate(want_all), act, "returned rows")
+    _say(f"  returned rows checked: {n_checked} of {int(kept_rows.sum())} kept, "
+         f"{int(dropped_rows.sum())} dropped at receive")
+    del got_all, want_all
 
     # --- output: the oracle's chain from x for the own pool's rows
     pool_self = np.zeros((scap, L))
