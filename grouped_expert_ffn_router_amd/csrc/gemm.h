@@ -186,8 +186,13 @@ __device__ __forceinline__ void put4(T* p, const float* v, int valid) {
     if (i < valid) p[i] = Act<T>::store(v[i]);
 }
 
+// Staged epilogue (STAGED = true): the MFMA kernel rounds the tile to
+// activations in LDS and stores whole row segments; row_dst(g, m) gives
+// element 0 of output row m (NULL: not stored) and the kernel writes
+// columns n0 .. n0 + BN - 1 (hidden units n0/2 .. for SwiGLU pairs).
 template <class T>
 struct ERouteDown {  // columns < E: fp32 logits (+bias); the rest: latent z
+  static constexpr bool STAGED = false;  // two output tensors of two types
   float* logits;
   T* z;
   const float* bias;
@@ -225,6 +230,7 @@ struct ERouteDown {  // columns < E: fp32 logits (+bias); the rest: latent z
 
 template <class T>
 struct ESwiGLU {  // hidden unit u of row m: act(silu(gate) * up)
+  static constexpr bool STAGED = true;
   T* out;
   int64_t ldo, group_stride;
   int col0;
@@ -245,6 +251,7 @@ struct ESwiGLU {  // hidden unit u of row m: act(silu(gate) * up)
   }
   struct Row { T* p; };
   __device__ Row row(int g, int m) const { return {dest(g, m)}; }
+  __device__ T* row_dst(int g, int m) const { return dest(g, m); }
   __device__ void store4_pair(const Row& r, int u, const float* gate, const float* up) const {
     if (!r.p) return;
     float h[4];
@@ -256,6 +263,7 @@ struct ESwiGLU {  // hidden unit u of row m: act(silu(gate) * up)
 
 template <class T>
 struct EScatter {  // row m of group g -> return row of receive row row_src[g][m]
+  static constexpr bool STAGED = true;
   char* ret;
   int64_t src_stride, row_bytes;
   int cap;
@@ -269,13 +277,16 @@ struct EScatter {  // row m of group g -> return row of receive row row_src[g][m
   __device__ void store(int g, int m, int n, float v) const { dest(g, m)[n] = Act<T>::store(v); }
   struct Row { T* p; };
   __device__ Row row(int g, int m) const { return {dest(g, m)}; }
+  __device__ T* row_dst(int g, int m) const { return dest(g, m); }
   __device__ void store4(const Row& r, int n, int N, const float* v) const { put4(r.p + n, v, N - n); }
 };
 
 template <class T>
 struct EStore {
+  static constexpr bool STAGED = true;
   T* out;
   int64_t ldo;
+  __device__ T* row_dst(int, int m) const { return out + (int64_t)m * ldo; }
   __device__ void store(int, int m, int n, float v) const { out[(int64_t)m * ldo + n] = Act<T>::store(v); }
   struct Row { T* p; };
   __device__ Row row(int, int m) const { return {out + (int64_t)m * ldo}; }
@@ -482,6 +493,62 @@ __device__ __forceinline__ void epilogue_row(const E& e, int g, int m, int M, in
   }
 }
 
+// Staged epilogue of a whole tile (all 512 threads; LDS free of the K loop's
+// operands).  Each lane rounds its accumulators (SwiGLU pairs first) to bf16
+// and writes them as 8-byte pieces into a row-major copy of the output tile
+// in LDS: OC output columns per row, the 16-byte chunks of a row XOR-swizzled
+// with the row index so that the 32 rows a write instruction touches fall in
+// different banks.  Then each wave stores 32 rows, 16 bytes per lane, whole
+// row segments (OC * 2 bytes) per group of lanes: every store instruction
+// writes full 128-byte lines, where the per-fragment pieces of the
+// accumulator layout would write 16 bytes of 32 different rows.  The values
+// and their rounding are those of the direct epilogue.
+template <class Cfg, bool GATEUP, class E>
+__device__ __forceinline__ void staged_epilogue(const E& e, int g, int m0, int n0, int M, int N, char* smem,
+                                                const f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, WTM = Cfg::WTM, WTN = Cfg::WTN, BM = Cfg::BM;
+  constexpr int OC = GATEUP ? Cfg::BN / 2 : Cfg::BN;  // output columns of the tile
+  constexpr int RB = OC * 2;                         // bytes of one staged row
+  constexpr int CH = RB / 16;                        // 16-byte chunks per row (a power of two)
+  static_assert(BM * RB <= 2 * Cfg::STAGE, "the staged tile fits the operand buffers");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3, frow = lane & 31, fhalf = lane >> 5;
+  __syncthreads();  // every wave is done reading operands (no loads are in flight here)
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int row = wm * WTM + i * 32 + frow;
+    char* lrow = smem + row * RB;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int j = 0; j < FN; j += (GATEUP ? 2 : 1)) {
+        const int n = wn * WTN + j * 32 + q * 8 + fhalf * 4;  // tile column (gate column for pairs)
+        const int oc = GATEUP ? (n >> 6) * 32 + (n & 31) : n;
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          v[t] = GATEUP ? silu(acc[i][j][q * 4 + t]) * acc[i][j + (GATEUP ? 1 : 0)][q * 4 + t] : acc[i][j][q * 4 + t];
+        const int byte = oc * 2;
+        *(uint2*)(lrow + (((byte >> 4) ^ (row & (CH - 1))) << 4) + (byte & 15)) = pack_bf16x4(v);
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int RPI = 64 / CH;  // rows per store instruction
+  const int col0 = (GATEUP ? n0 / 2 : n0), ncols = GATEUP ? N / 2 : N;
+  const int c = lane % CH;
+#pragma unroll 4
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int row = wave * 32 + it * RPI + lane / CH;
+    const uint4 d = *(const uint4*)(smem + row * RB + ((c ^ (row & (CH - 1))) << 4));
+    const int m = m0 + row;
+    if (m < M && col0 + c * 8 < ncols) {
+      bf16_t* p = e.row_dst(g, m);
+      if (p) *(uint4*)(p + col0 + c * 8) = d;
+    }
+  }
+}
+
 // Partial tile layout: float4 chunk c (0..31, = (i*FN + j)*4 + v/4) of thread
 // tid at float offset (c * 512 + tid) * 4 of the slot (coalesced).
 constexpr int PART_FLOATS = 256 * 256;
@@ -674,9 +741,13 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int groups, int tiles_n, int P, floa
               make_float4(acc[i][j][v * 4], acc[i][j][v * 4 + 1], acc[i][j][v * 4 + 2], acc[i][j][v * 4 + 3]);
     return;
   }
+  if constexpr (E::STAGED) {
+    staged_epilogue<Cfg, GATEUP>(e, g, m0, n0, M, N, smem, acc);
+  } else {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
-    epilogue_row<GATEUP, FN>(e, g, m0 + wm * WTM + i * 32 + frow, M, n0 + wn * WTN, N, fhalf, acc[i]);
+    for (int i = 0; i < FM; ++i)
+      epilogue_row<GATEUP, FN>(e, g, m0 + wm * WTM + i * 32 + frow, M, n0 + wn * WTN, N, fhalf, acc[i]);
+  }
 }
 
 // Tail tiles of a gemm_bf16_mfma launch with the same arguments: adds each
