@@ -187,8 +187,10 @@ __device__ __forceinline__ void put4(T* p, const float* v, int valid) {
 }
 
 // Staged epilogue (STAGED = true): the MFMA kernel rounds the tile to
-// activations in LDS and stores whole row segments; row_dst(g, m) gives
-// element 0 of output row m (NULL: not stored) and the kernel writes
+// activations in LDS and stores whole row segments.  row_key(g, m), which may
+// read memory, is taken for every row of the tile when the tile starts (its
+// latency hides behind the K loop); key_dst(key), which reads nothing, gives
+// element 0 of the output row (NULL: not stored), and the kernel writes
 // columns n0 .. n0 + BN - 1 (hidden units n0/2 .. for SwiGLU pairs).
 template <class T>
 struct ERouteDown {  // columns < E: fp32 logits (+bias); the rest: latent z
@@ -251,7 +253,12 @@ struct ESwiGLU {  // hidden unit u of row m: act(silu(gate) * up)
   }
   struct Row { T* p; };
   __device__ Row row(int g, int m) const { return {dest(g, m)}; }
-  __device__ T* row_dst(int g, int m) const { return dest(g, m); }
+  // staged epilogue: element offset of row m's first hidden unit, -1: not stored
+  __device__ int64_t row_key(int g, int m) const {
+    const T* p = dest(g, m);
+    return p ? (int64_t)(p - out) : -1;
+  }
+  __device__ T* key_dst(int64_t key) const { return key < 0 ? nullptr : out + key; }
   __device__ void store4_pair(const Row& r, int u, const float* gate, const float* up) const {
     if (!r.p) return;
     float h[4];
@@ -277,7 +284,12 @@ struct EScatter {  // row m of group g -> return row of receive row row_src[g][m
   __device__ void store(int g, int m, int n, float v) const { dest(g, m)[n] = Act<T>::store(v); }
   struct Row { T* p; };
   __device__ Row row(int g, int m) const { return {dest(g, m)}; }
-  __device__ T* row_dst(int g, int m) const { return dest(g, m); }
+  // staged epilogue: the receive row (s * cap + slot) whose return row row m fills
+  __device__ int64_t row_key(int g, int m) const { return row_src[g * rs_stride + m]; }
+  __device__ T* key_dst(int64_t key) const {
+    const int rs = (int)key, s = rs / cap, sl = rs - s * cap;
+    return (T*)(ret + s * src_stride + (int64_t)sl * row_bytes);
+  }
   __device__ void store4(const Row& r, int n, int N, const float* v) const { put4(r.p + n, v, N - n); }
 };
 
@@ -286,7 +298,8 @@ struct EStore {
   static constexpr bool STAGED = true;
   T* out;
   int64_t ldo;
-  __device__ T* row_dst(int, int m) const { return out + (int64_t)m * ldo; }
+  __device__ int64_t row_key(int, int m) const { return m; }
+  __device__ T* key_dst(int64_t key) const { return out + key * ldo; }
   __device__ void store(int, int m, int n, float v) const { out[(int64_t)m * ldo + n] = Act<T>::store(v); }
   struct Row { T* p; };
   __device__ Row row(int, int m) const { return {out + (int64_t)m * ldo}; }
@@ -504,7 +517,8 @@ __device__ __forceinline__ void epilogue_row(const E& e, int g, int m, int M, in
 // accumulator layout would write 16 bytes of 32 different rows.  The values
 // and their rounding are those of the direct epilogue.
 template <class Cfg, bool GATEUP, class E>
-__device__ __forceinline__ void staged_epilogue(const E& e, int g, int m0, int n0, int M, int N, char* smem,
+__device__ __forceinline__ void staged_epilogue(const E& e, int m0, int n0, int M, int N, char* smem,
+                                                int64_t* keys, int64_t my_key,
                                                 const f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
   constexpr int FM = Cfg::FM, FN = Cfg::FN, WTM = Cfg::WTM, WTN = Cfg::WTN, BM = Cfg::BM;
   constexpr int OC = GATEUP ? Cfg::BN / 2 : Cfg::BN;  // output columns of the tile
@@ -513,6 +527,7 @@ __device__ __forceinline__ void staged_epilogue(const E& e, int g, int m0, int n
   static_assert(BM * RB <= 2 * Cfg::STAGE, "the staged tile fits the operand buffers");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3, frow = lane & 31, fhalf = lane >> 5;
+  if (tid < BM) keys[tid] = my_key;  // taken when the tile started
   __syncthreads();  // every wave is done reading operands (no loads are in flight here)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -541,9 +556,8 @@ __device__ __forceinline__ void staged_epilogue(const E& e, int g, int m0, int n
   for (int it = 0; it < 32 / RPI; ++it) {
     const int row = wave * 32 + it * RPI + lane / CH;
     const uint4 d = *(const uint4*)(smem + row * RB + ((c ^ (row & (CH - 1))) << 4));
-    const int m = m0 + row;
-    if (m < M && col0 + c * 8 < ncols) {
-      bf16_t* p = e.row_dst(g, m);
+    if (m0 + row < M && col0 + c * 8 < ncols) {
+      bf16_t* p = e.key_dst(keys[row]);
       if (p) *(uint4*)(p + col0 + c * 8) = d;
     }
   }
@@ -575,6 +589,12 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int groups, int tiles_n, int P, floa
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
+  // the staged epilogue's row keys (e.g. a scatter's row lookups), read now
+  // so that their latency hides behind the K loop
+  __shared__ int64_t keys[E::STAGED ? BM : 1];
+  int64_t my_key = -1;
+  if constexpr (E::STAGED)
+    if (slot < 0 && tid < BM && m0 + tid < M) my_key = e.row_key(g, m0 + tid);
 
   // wave w owns the 4 LDS blocks (1 KB = 8 rows) w*4 .. w*4+3 of A and of B:
   // slot d holds rows w*32 + d*8 + lane/8, lane lands at block + 16*lane.
@@ -742,7 +762,7 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int groups, int tiles_n, int P, floa
     return;
   }
   if constexpr (E::STAGED) {
-    staged_epilogue<Cfg, GATEUP>(e, g, m0, n0, M, N, smem, acc);
+    staged_epilogue<Cfg, GATEUP>(e, m0, n0, M, N, smem, keys, my_key, acc);
   } else {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
