@@ -217,13 +217,14 @@ def _cpu_model():
 SWEEP_FACTORS = [(110, 115), (100, 115), (125, 115), (150, 115), (110, 100), (110, 130), (110, 150)]
 
 
-VENDOR_SHAPES = [(22528, 3072, 3072), (8192, 6144, 6144), (8192, 6144, 3072), (8192, 3456, 6144)]
+VENDOR_SHAPES = [(22528, 3072, 3072), (8192, 6144, 6144), (8192, 6144, 3072), (8192, 3456, 6144),
+                 (22528, 3072, 1536)]
 
 
 def vendor_gemm(args):
     """torch.matmul in bf16 (the vendor library) on M x N x K shapes of the layer:
     one expert wave's gate/up rows as one dense GEMM, the shared gate/up, the
-    up-projection + shared down, the route GEMM.  B is a transposed view of an
+    up-projection + shared down, the route GEMM, one expert wave's down rows.  B is a transposed view of an
     [N][K] matrix (2-D matmul, no batching)."""
     import torch
     torch.manual_seed(args.seed)
