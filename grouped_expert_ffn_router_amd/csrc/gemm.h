@@ -194,7 +194,10 @@ __device__ __forceinline__ void put4(T* p, const float* v, int valid) {
 // columns n0 .. n0 + BN - 1 (hidden units n0/2 .. for SwiGLU pairs).
 template <class T>
 struct ERouteDown {  // columns < E: fp32 logits (+bias); the rest: latent z
-  static constexpr bool STAGED = false;  // two output tensors of two types
+  // tiles of latent columns only go through the staged epilogue (E a
+  // multiple of 8 keeps their 16-byte pieces aligned); tiles holding logits
+  // store from registers
+  static constexpr bool STAGED = true;
   float* logits;
   T* z;
   const float* bias;
@@ -219,6 +222,10 @@ struct ERouteDown {  // columns < E: fp32 logits (+bias); the rest: latent z
     return {logits + (int64_t)m * E, z + (int64_t)m * L,
             bias ? bias + (int64_t)(bias_row_tokens ? m / bias_row_tokens : 0) * E : nullptr};
   }
+  __device__ bool staged_tile(int n0) const { return n0 >= E && (E & 7) == 0; }
+  __device__ int64_t row_key(int, int m) const { return m; }
+  // element 0 of the row in output-column numbering: column n >= E lands at z[m][n - E]
+  __device__ T* key_dst(int64_t key) const { return z + key * L - E; }
   __device__ void store4(const Row& r, int n, int N, const float* v) const {
     if (n < E) {
       float b[4] = {0.f, 0.f, 0.f, 0.f};
@@ -253,6 +260,7 @@ struct ESwiGLU {  // hidden unit u of row m: act(silu(gate) * up)
   }
   struct Row { T* p; };
   __device__ Row row(int g, int m) const { return {dest(g, m)}; }
+  __device__ bool staged_tile(int) const { return true; }
   // staged epilogue: element offset of row m's first hidden unit, -1: not stored
   __device__ int64_t row_key(int g, int m) const {
     const T* p = dest(g, m);
@@ -284,6 +292,7 @@ struct EScatter {  // row m of group g -> return row of receive row row_src[g][m
   __device__ void store(int g, int m, int n, float v) const { dest(g, m)[n] = Act<T>::store(v); }
   struct Row { T* p; };
   __device__ Row row(int g, int m) const { return {dest(g, m)}; }
+  __device__ bool staged_tile(int) const { return true; }
   // staged epilogue: the receive row (s * cap + slot) whose return row row m fills
   __device__ int64_t row_key(int g, int m) const { return row_src[g * rs_stride + m]; }
   __device__ T* key_dst(int64_t key) const {
@@ -298,6 +307,7 @@ struct EStore {
   static constexpr bool STAGED = true;
   T* out;
   int64_t ldo;
+  __device__ bool staged_tile(int) const { return true; }
   __device__ int64_t row_key(int, int m) const { return m; }
   __device__ T* key_dst(int64_t key) const { return out + key * ldo; }
   __device__ void store(int, int m, int n, float v) const { out[(int64_t)m * ldo + n] = Act<T>::store(v); }
@@ -593,8 +603,11 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int groups, int tiles_n, int P, floa
   // so that their latency hides behind the K loop
   __shared__ int64_t keys[E::STAGED ? BM : 1];
   int64_t my_key = -1;
-  if constexpr (E::STAGED)
-    if (slot < 0 && tid < BM && m0 + tid < M) my_key = e.row_key(g, m0 + tid);
+  bool staged = false;
+  if constexpr (E::STAGED) {
+    staged = slot < 0 && e.staged_tile(n0);
+    if (staged && tid < BM && m0 + tid < M) my_key = e.row_key(g, m0 + tid);
+  }
 
   // wave w owns the 4 LDS blocks (1 KB = 8 rows) w*4 .. w*4+3 of A and of B:
   // slot d holds rows w*32 + d*8 + lane/8, lane lands at block + 16*lane.
@@ -761,8 +774,8 @@ gemm_bf16_mfma(A a, B b, E e, int N, int K, int groups, int tiles_n, int P, floa
               make_float4(acc[i][j][v * 4], acc[i][j][v * 4 + 1], acc[i][j][v * 4 + 2], acc[i][j][v * 4 + 3]);
     return;
   }
-  if constexpr (E::STAGED) {
-    staged_epilogue<Cfg, GATEUP>(e, m0, n0, M, N, smem, keys, my_key, acc);
+  if (staged) {  // uniform per workgroup
+    if constexpr (E::STAGED) staged_epilogue<Cfg, GATEUP>(e, m0, n0, M, N, smem, keys, my_key, acc);
   } else {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
