@@ -41,8 +41,9 @@ int hip_fail(hipError_t e, const char* where) {
   } while (0)
 
 // ---------------------------------------------------------------- kernel timing
-// While enabled, every launch is bracketed by two HIP events recorded on the
-// launch stream (moe_timing_enable / moe_timing_read).
+// While enabled, every launch carries two HIP events that its own dispatch
+// records as the kernel starts and ends (moe_timing_enable / moe_timing_read;
+// see launch() in moe_internal.h).
 
 struct TimingRec {
   const char* name;
@@ -71,6 +72,17 @@ Timing& timing() {
   return t;
 }
 
+}  // namespace
+
+namespace moe {
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace moe
+
+namespace {
+
 class KernelTimer {  // scope guard around one launch
  public:
   KernelTimer(const char* name, hipStream_t st) : st_(st) {
@@ -80,20 +92,24 @@ class KernelTimer {  // scope guard around one launch
     rec_.name = name;
     rec_.start = t.get();
     rec_.stop = t.get();
-    if (!rec_.start || !rec_.stop || hipEventRecord(rec_.start, st) != hipSuccess) {
+    if (!rec_.start || !rec_.stop) {
       if (rec_.start) t.pool.push_back(rec_.start);
       if (rec_.stop) t.pool.push_back(rec_.stop);
       return;
     }
+    launch_events() = LaunchEvents{rec_.start, rec_.stop};  // the next launch records them
     armed_ = true;
   }
   ~KernelTimer() {
     if (!armed_) return;
+    LaunchEvents& ev = launch_events();
+    const bool launched = ev.start == nullptr;  // a launch took the pair
+    ev = LaunchEvents{};
     Timing& t = timing();
     std::lock_guard<std::mutex> g(t.mu);
-    if (hipEventRecord(rec_.stop, st_) == hipSuccess) {
+    if (launched) {
       t.recs.push_back(rec_);
-    } else {
+    } else {  // nothing was launched (an empty batch)
       t.pool.push_back(rec_.start);
       t.pool.push_back(rec_.stop);
     }
@@ -275,14 +291,14 @@ hipError_t gemm_bf16(const char* name, const char* fixup_name, A a, B b, E e, in
   }
   {
     KernelTimer kt(name, st);
-    hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, GATEUP, A, B, E>), dim3((unsigned)gemm_grid(max_tiles, P)), dim3(Cfg::NT), 0,
+    launch((gemm_bf16_mfma<Cfg, GATEUP, A, B, E>), dim3((unsigned)gemm_grid(max_tiles, P)), dim3(Cfg::NT), 0,
                        st, a, b, e, N, K, groups, (int)tiles_n, P, split ? part : nullptr);
     hipError_t r = hipGetLastError();
     if (r != hipSuccess) return r;
   }
   if (!split) return hipSuccess;
   KernelTimer kt(fixup_name, st);
-  hipLaunchKernelGGL((gemm_bf16_fixup<Cfg, GATEUP, A, E>), dim3(2048u), dim3(64), 0, st, a, e,
+  launch((gemm_bf16_fixup<Cfg, GATEUP, A, E>), dim3(2048u), dim3(64), 0, st, a, e,
                      N, K, groups, (int)tiles_n, P, (const float*)part);
   return hipGetLastError();
 }
@@ -293,7 +309,7 @@ hipError_t gemm_f32(const char* name, A a, B b, E e, int N, int K, int64_t max_r
   if (cols <= 0 || max_rows <= 0 || groups <= 0) return hipSuccess;
   KernelTimer kt(name, st);
   const dim3 grid((unsigned)ceil_div(cols, 16), (unsigned)ceil_div(max_rows, 16), (unsigned)groups);
-  hipLaunchKernelGGL((gemm_f32_simple<GATEUP, A, B, E>), grid, dim3(16, 16), 0, st, a, b, e, N, K);
+  launch((gemm_f32_simple<GATEUP, A, B, E>), grid, dim3(16, 16), 0, st, a, b, e, N, K);
   return hipGetLastError();
 }
 

@@ -108,7 +108,7 @@ hipError_t launch_select_topk(const float* logits, int T, int E, int k, int32_t*
   const int epl = (E + 63) / 64;
   const dim3 grid((unsigned)((T + 3) / 4)), block(256);
   if (T == 0) return hipSuccess;
-#define SEL(N) hipLaunchKernelGGL(select_topk_kernel<N>, grid, block, 0, st, logits, T, E, k, idx, w)
+#define SEL(N) launch(select_topk_kernel<N>, grid, block, 0, st, logits, T, E, k, idx, w)
   if (epl <= 1) SEL(1);
   else if (epl <= 2) SEL(2);
   else if (epl <= 4) SEL(4);
@@ -228,7 +228,7 @@ hipError_t launch_send_rank(const int32_t* idx, int n_assign, int X, int E, int 
                             int32_t* chunk_count, hipStream_t st) {
   const int nch = (n_assign + SCAN_CHUNK - 1) / SCAN_CHUNK;
   if (nch == 0) return hipSuccess;
-  hipLaunchKernelGGL(send_rank_kernel, dim3(nch), dim3(256), 4 * (R + 1) * sizeof(int32_t), st, idx, n_assign,
+  launch(send_rank_kernel, dim3(nch), dim3(256), 4 * (R + 1) * sizeof(int32_t), st, idx, n_assign,
                      X, E, R, local_rank, chunk_count, nch);
   return hipGetLastError();
 }
@@ -257,7 +257,7 @@ send_scan_kernel(const int32_t* __restrict__ chunk_count, int nch, int R, int ca
 hipError_t launch_send_scan(const int32_t* chunk_count, int nch, int R, int cap, int32_t* chunk_base, int32_t* ctr,
                             int32_t* send_count_out, hipStream_t st) {
   // nch == 0 (no tokens) still runs: every column total is 0
-  hipLaunchKernelGGL(send_scan_kernel, dim3(R + 1), dim3(256), 0, st, chunk_count, nch, R, cap, chunk_base, ctr,
+  launch(send_scan_kernel, dim3(R + 1), dim3(256), 0, st, chunk_count, nch, R, cap, chunk_base, ctr,
                      send_count_out);
   return hipGetLastError();
 }
@@ -271,7 +271,7 @@ ragged_offsets_kernel(const int32_t* __restrict__ send_count, int R, int32_t* __
 }
 
 hipError_t launch_ragged_offsets(const int32_t* send_count, int R, int32_t* send_off, hipStream_t st) {
-  hipLaunchKernelGGL(ragged_offsets_kernel, dim3(1), dim3(256), 0, st, send_count, R, send_off);
+  launch(ragged_offsets_kernel, dim3(1), dim3(256), 0, st, send_count, R, send_off);
   return hipGetLastError();
 }
 
@@ -355,7 +355,7 @@ hipError_t launch_pack(const void* z, int64_t row_bytes, const int32_t* idx, con
   const int64_t fill_blocks = ragged_off ? 0 : ((int64_t)R * cap * tail + PACK_TPB - 1) / PACK_TPB;
   const int64_t blocks = (int64_t)T + fill_blocks;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(PACK_TPB), 0, st, (const char*)z, row_bytes, idx,
+  launch(pack_kernel, dim3((unsigned)blocks), dim3(PACK_TPB), 0, st, (const char*)z, row_bytes, idx,
                      local_rank, chunk_base, nch, T, k, X, E, R, cap, (char*)pools, dst_stride, prow, slot_of,
                      send_count, ragged_off, ctr);
   return hipGetLastError();
@@ -384,7 +384,7 @@ hipError_t launch_recv_rank(const void* pools, int64_t src_stride, int64_t prow,
   const int n_rows = R * cap;
   const int nch = (n_rows + SCAN_CHUNK - 1) / SCAN_CHUNK;
   if (nch == 0) return hipSuccess;
-  hipLaunchKernelGGL(recv_rank_kernel, dim3(nch), dim3(256), 4 * (X + 1) * sizeof(int32_t), st,
+  launch(recv_rank_kernel, dim3(nch), dim3(256), 4 * (X + 1) * sizeof(int32_t), st,
                      (const char*)pools, src_stride, prow, id_off, n_rows, cap, X, my_rank, row_j, row_lrank,
                      chunk_count, nch);
   return hipGetLastError();
@@ -411,7 +411,7 @@ recv_scan_kernel(const int32_t* __restrict__ chunk_count, int nch, int X, int rc
 
 hipError_t launch_recv_scan(const int32_t* chunk_count, int nch, int X, int rcap, int32_t* chunk_base,
                             int32_t* arrivals, int32_t* kept, int32_t* ctr, hipStream_t st) {
-  hipLaunchKernelGGL(recv_scan_kernel, dim3(X + 1), dim3(256), 0, st, chunk_count, nch, X, rcap, chunk_base, arrivals,
+  launch(recv_scan_kernel, dim3(X + 1), dim3(256), 0, st, chunk_count, nch, X, rcap, chunk_base, arrivals,
                      kept, ctr);
   return hipGetLastError();
 }
@@ -432,7 +432,7 @@ hipError_t launch_recv_final(const int32_t* row_j, const int32_t* row_lrank, con
                              int X, int32_t* row_rank, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
   const int nch = (n_rows + SCAN_CHUNK - 1) / SCAN_CHUNK;
-  hipLaunchKernelGGL(recv_final_kernel, dim3((n_rows + 255) / 256), dim3(256), 0, st, row_j, row_lrank, chunk_base,
+  launch(recv_final_kernel, dim3((n_rows + 255) / 256), dim3(256), 0, st, row_j, row_lrank, chunk_base,
                      nch, n_rows, X, row_rank);
   return hipGetLastError();
 }
@@ -471,7 +471,7 @@ hipError_t launch_recv_place(const int32_t* row_j, const int32_t* row_rank, cons
                              int32_t* ctr, hipStream_t st) {
   const int n = max(max(n_rows, nj * rcap), nj);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(recv_place_kernel, dim3((n + 255) / 256), dim3(256), 0, st, row_j, row_rank, kept, n_rows, rcap,
+  launch(recv_place_kernel, dim3((n + 255) / 256), dim3(256), 0, st, row_j, row_rank, kept, n_rows, rcap,
                      j0, nj, wave_rows, wave_count, row_src, ctr);
   return hipGetLastError();
 }
@@ -498,7 +498,7 @@ hipError_t launch_wave_gather(const void* pools, int64_t src_stride, int64_t pro
                               hipStream_t st) {
   const int64_t rows = (int64_t)nj * rcap;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(wave_gather_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, (const char*)pools,
+  launch(wave_gather_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, (const char*)pools,
                      src_stride, prow, cap, row_bytes, row_src, wave_count, nj, rcap, (char*)wave_buf);
   return hipGetLastError();
 }
@@ -530,7 +530,7 @@ zero_dropped_kernel(const int32_t* __restrict__ row_j, const int32_t* __restrict
 hipError_t launch_zero_dropped(const int32_t* row_j, const int32_t* row_rank, int n_rows, int cap, int rcap, int j0,
                                int nj, void* ret, int64_t ret_src_stride, int64_t row_bytes, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_dropped_kernel, dim3((n_rows + 255) / 256), dim3(256), 0, st, row_j, row_rank, n_rows, cap,
+  launch(zero_dropped_kernel, dim3((n_rows + 255) / 256), dim3(256), 0, st, row_j, row_rank, n_rows, cap,
                      rcap, j0, nj, (char*)ret, ret_src_stride, row_bytes);
   return hipGetLastError();
 }
@@ -638,10 +638,10 @@ hipError_t launch_combine(int act, const void* ret, int64_t dst_stride, int64_t 
                           int32_t* ctr, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (act == 0)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(COMBINE_TPB), 0, st, (const char*)ret, dst_stride,
+    launch(combine_kernel<bf16_t>, dim3(T), dim3(COMBINE_TPB), 0, st, (const char*)ret, dst_stride,
                        row_bytes, cap, R, slot_of, w, k, L, (bf16_t*)c_out, ldc, ctr);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(COMBINE_TPB), 0, st, (const char*)ret, dst_stride,
+    launch(combine_kernel<float>, dim3(T), dim3(COMBINE_TPB), 0, st, (const char*)ret, dst_stride,
                        row_bytes, cap, R, slot_of, w, k, L, (float*)c_out, ldc, ctr);
   return hipGetLastError();
 }

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace moe {
@@ -38,6 +39,27 @@ struct Ctr {
   do {                                 \
   } while (0)
 #endif
+
+// Kernel timing (moe_timing_enable): the host side of a timed launch sets a
+// pair of events here, and the launch below hands them to the dispatch itself
+// (hipExtLaunchKernel), which records them as the kernel starts and ends, so
+// the pair brackets the kernel alone.  Thread-local; a launch consumes the pair.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+template <class F, class... Args>
+void launch(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st, Args... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.start) {
+    const LaunchEvents e = ev;
+    ev = LaunchEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, e.start, e.stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+  }
+}
 
 hipError_t launch_select_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                               hipStream_t st);

@@ -283,9 +283,10 @@ const char* moe_last_error(void);
 
 /* Per-kernel timing, a measurement aid for the layer above (not part of the
  * layer's arithmetic).  While enabled, every kernel launched by the calls
- * above is bracketed by two HIP events recorded on the stream it is launched
- * on, so the elapsed time between them is that kernel's duration on its own
- * stream.  Enabling adds two event records per launch; results are unchanged.
+ * above carries two HIP events that its own dispatch records as the kernel
+ * starts and ends (hipExtLaunchKernel), so the elapsed time between them is
+ * that kernel's duration on its stream, with no marker packets between
+ * kernels.  Results are unchanged.
  * Labels: route_gemm, select_topk, send_rank, send_scan, ragged_offsets, pack, recv_rank,
  * recv_scan, recv_final, recv_place, wave_gather, expert_gate_up, expert_down,
  * zero_dropped, combine, shared_gate_up, up_shared_down, and the tail-split
