@@ -879,6 +879,53 @@ def test_live_waves_same_bits(runner):
     assert sizes[1]["workspace_bytes"] < sizes[2]["workspace_bytes"] < sizes[3]["workspace_bytes"]
 
 
+def test_graph_replay_same_bits(runner):
+    """The two-stream step (shared experts and odd waves on a second stream)
+    captured once as a HIP graph: every replay, with eager steps and
+    synchronisations between replays, gives the eager step's bytes.  The step
+    allocates nothing, clears nothing with memsets and never waits on the
+    host, so it can run under capture."""
+    from concurrent.futures import ThreadPoolExecutor
+    sh = configs.get(3)
+    scap, _ = O.capacities(sh)
+    _say("[graph replay] config 3, two streams, three replays")
+    inp = gen.generate(sh, seed=5, send_cap=scap)
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        drawn = dict(zip(range(sh.n_ranks), ex.map(inp["sources"], range(sh.n_ranks))))
+    inp["sources"] = drawn.__getitem__
+    lay = runner.OneRankLayer(sh, inp, gather="fused", live_waves=2)
+    names = ("out", "z", "logits", "ret_send", "slot_of", "row_src", "wave_count")
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [host(getattr(lay, n)).view(np.uint8).copy() for n in names]
+
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(2):
+        lay.run(main, side)
+    want = snapshot()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(main)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        lay.run(cap, side)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for n in ("out", "z", "logits", "ret_send"):  # the replay has to write them again
+            getattr(lay, n).zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cap):
+            g.replay()
+        for a, b, n in zip(snapshot(), want, names):
+            assert np.array_equal(a, b), f"replay {i}: {n} differs from the eager step"
+        lay.run(main, side)
+        for a, b, n in zip(snapshot(), want, names):
+            assert np.array_equal(a, b), f"eager step after replay {i}: {n} differs"
+    del g, lay
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_one_rank_ragged_full_size(runner, cfg):
     """The ragged dropless layer at one rank's real shape against the fixed-pool
