@@ -681,10 +681,9 @@ def test_one_rank_full_size_bench_inputs(runner, cfg):
         max-abs error both reported; the raw error is asserted within
         2e-2 RMS too.
     Config 5 (65,536 tokens; the other ranks' pools are drawn inputs, not
-    routed): the received pools must equal those inputs byte for byte, and
-    the returned rows are checked element by element for every row of the
-    rank's own pool plus 2,048 sampled rows of each expert (its 500,000 rows
-    would take the float64 oracle minutes); everything else as above."""
+    routed): the received pools must equal those inputs byte for byte;
+    everything else as above, all 566k returned rows included (compared in
+    chunks of 16,384 rows)."""
     from concurrent.futures import ThreadPoolExecutor
     sh = _full_size_shape(cfg)
     scap, rcap = O.capacities(sh)
@@ -799,30 +798,20 @@ def test_one_rank_full_size_bench_inputs(runner, cfg):
     if drop_idx.size:
         assert not torch.any(flat_ret[torch.as_tensor(drop_idx, device=flat_ret.device)] != 0).item(), \
             "a receive-dropped row returned nonzero values"
-    pick = []          # (expert, pool rows) to compare
-    for j in range(X):
-        q = rv["row_src"][j, :int(rv["count"][j])].astype(np.int64)
-        if routed:
-            pick.append((j, q))
-        else:
-            own_q = q[q // scap == r]
-            samp = rng.choice(q, min(q.size, 2048), replace=False) if q.size else q
-            pick.append((j, np.unique(np.concatenate([own_q, samp]))))
     flat_pool = lay.recv_pools.view(R * scap, -1)
     n_checked = 0
-    got_all, want_all = [], []
-    for j, q in pick:
-        if not q.size:
-            continue
-        qd = torch.as_tensor(q, device=flat_pool.device)
-        _, rows_j = _decode_pools(flat_pool[qd], L, act)
-        want_all.append(O.expert_ffn(rows_j, inp["w13"][j], inp["w2"][j], H, act))
-        got_all.append(host(flat_ret[qd]))
-        n_checked += q.size
-    assert_stored_close(np.concatenate(got_all), np.concatenate(want_all), act, "returned rows")
-    _say(f"  returned rows checked: {n_checked} of {int(kept_rows.sum())} kept, "
-         f"{int(dropped_rows.sum())} dropped at receive")
-    del got_all, want_all
+    CH = 16384  # rows per comparison, so that config 5's 566k rows stay within a few GB of host memory
+    for j in range(X):
+        q = rv["row_src"][j, :int(rv["count"][j])].astype(np.int64)
+        for c0 in range(0, q.size, CH):
+            qd = torch.as_tensor(q[c0:c0 + CH], device=flat_pool.device)
+            _, rows_j = _decode_pools(flat_pool[qd], L, act)
+            want = O.expert_ffn(rows_j, inp["w13"][j], inp["w2"][j], H, act)
+            assert_stored_close(host(flat_ret[qd]), want, act, f"returned rows of expert {j}, rows {c0}..")
+            n_checked += qd.numel()
+            del rows_j, want
+    assert n_checked == int(kept_rows.sum())
+    _say(f"  returned rows checked: all {n_checked} kept, {int(dropped_rows.sum())} dropped at receive")
 
     # --- output: the oracle's chain from x for the own pool's rows
     pool_self = np.zeros((scap, L))
