@@ -36,6 +36,24 @@ def upload(arr, device):
     raise TypeError(f"unsupported host dtype {a.dtype}")
 
 
+def rank_blocks(R, shape, dtype, device):
+    """An [R][*shape] tensor whose per-rank blocks each start 256-byte aligned
+    (the library takes 16-byte aligned activation pointers; a plain [R][T][n]
+    tensor puts rank r at r*T*n elements, unaligned for odd widths)."""
+    n = int(np.prod(shape))
+    es = torch.empty((), dtype=dtype).element_size()
+    stride = -(-n * es // 256) * 256 // es
+    return torch.empty((R, stride), dtype=dtype, device=device)[:, :n].unflatten(1, tuple(shape))
+
+
+def upload_rank_blocks(arr, device):
+    """upload() of a host [R][...] array into 256-byte aligned per-rank blocks."""
+    t = upload(arr, device)
+    out = rank_blocks(t.shape[0], t.shape[1:], t.dtype, device)
+    out.copy_(t)
+    return out
+
+
 def _act(shape):
     return torch.bfloat16 if shape.act == "bf16" else torch.float32
 
@@ -406,7 +424,7 @@ class AllRanksLayer:
         dev = device
         self.dims = [B.make_dims(shape, my_rank=r) for r in range(R)]
         self.scap, self.rcap, self.prow = B.capacity(self.dims[0])
-        self.x = upload(inp["x"], dev)                                  # [R][T][D]
+        self.x = upload_rank_blocks(inp["x"], dev)                      # [R][T][D]
         self.w_router = upload(inp["w_router"], dev)
         self.w_down = upload(inp["w_down"], dev)
         bias = inp["bias"]
@@ -419,7 +437,7 @@ class AllRanksLayer:
         self.w_up = upload(inp["w_up"], dev)
         self.ws13 = upload(inp["ws13"], dev)
         self.ws2 = upload(inp["ws2"], dev)
-        self.logits = torch.empty((R, T, E), dtype=torch.float32, device=dev)
+        self.logits = rank_blocks(R, (T, E), torch.float32, dev)
         self.z = torch.empty((R, T, L), dtype=act, device=dev)
         self.idx = torch.empty((R, T, k), dtype=torch.int32, device=dev)
         self.w = torch.empty((R, T, k), dtype=torch.float32, device=dev)
@@ -432,7 +450,7 @@ class AllRanksLayer:
         self.wave_buf = (torch.empty((R, W, WX, self.rcap, L), dtype=act, device=dev) if gather == "buffer"
                          else None)
         self.ret = torch.zeros((R, R, self.scap, L), dtype=act, device=dev)                     # [recv][src]
-        self.out = torch.empty((R, T, D), dtype=act, device=dev)
+        self.out = rank_blocks(R, (T, D), act, dev)
         self.ws = [torch.empty((B.workspace_size(self.dims[0]),), dtype=torch.uint8, device=dev)
                    for _ in range(R)]
 
@@ -507,7 +525,7 @@ class RaggedAllRanksLayer:
         self.send_dims = [B.make_dims(exact_fit(shape, 1, 1), my_rank=r) for r in range(R)]
         self.rcap = self.expert_rows
         self.prow = B.capacity(self.send_dims[0])[2]
-        self.x = upload(inp["x"], dev)
+        self.x = upload_rank_blocks(inp["x"], dev)
         self.w_router = upload(inp["w_router"], dev)
         self.w_down = upload(inp["w_down"], dev)
         bias = inp["bias"]
@@ -520,7 +538,7 @@ class RaggedAllRanksLayer:
         self.w_up = upload(inp["w_up"], dev)
         self.ws13 = upload(inp["ws13"], dev)
         self.ws2 = upload(inp["ws2"], dev)
-        self.logits = torch.empty((R, T, E), dtype=torch.float32, device=dev)
+        self.logits = rank_blocks(R, (T, E), torch.float32, dev)
         self.z = torch.empty((R, T, L), dtype=act, device=dev)
         self.idx = torch.empty((R, T, k), dtype=torch.int32, device=dev)
         self.w = torch.empty((R, T, k), dtype=torch.float32, device=dev)
@@ -532,7 +550,7 @@ class RaggedAllRanksLayer:
         self.row_src = torch.empty((R, W, WX, self.rcap), dtype=torch.int32, device=dev)
         self.wave_count = torch.empty((R, W, WX), dtype=torch.int32, device=dev)
         self.wave_buf = torch.empty((WX, self.rcap, L), dtype=act, device=dev) if gather == "buffer" else None
-        self.out = torch.empty((R, T, D), dtype=act, device=dev)
+        self.out = rank_blocks(R, (T, D), act, dev)
         self.ws_send = [torch.zeros((B.workspace_size(d),), dtype=torch.uint8, device=dev) for d in self.send_dims]
         self.recv_dims, self.recv, self.ret, self.ws_recv, self.seg_off = [], [], [], [], []
 

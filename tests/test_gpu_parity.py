@@ -373,6 +373,52 @@ def test_all_ranks_max_top_k(runner):
     _check_all_ranks(sh, inp, ref, lay, True)
 
 
+def _random_shape(i):
+    """A small all-ranks shape drawn from a seeded generator: 2-8 ranks, 1-6
+    local experts in 1-3 waves, top-1..6, up to 400 tokens, 0-2 shared experts,
+    capacity factors 1.00-1.60, every width a multiple of 64 (bf16) or ragged
+    (float32, every third shape)."""
+    rng = np.random.default_rng(1000 + i)
+    f32 = i % 3 == 2
+    while True:
+        R = int(rng.choice([2, 3, 4, 6, 8]))
+        X = int(rng.choice([1, 2, 3, 4, 6]))
+        E = R * X
+        if not f32 and E % 4:
+            continue
+        W = int(rng.choice([w for w in (1, 2, 3) if X % w == 0]))
+        k = int(rng.integers(1, min(6, E) + 1))
+        break
+    T = int(rng.integers(1, 400))
+    S = int(rng.integers(0, 3))
+    if f32:
+        D, L = int(rng.integers(8, 100)), 8 * int(rng.integers(1, 9))
+        H, HS = int(rng.integers(4, 41)), 4 * int(rng.integers(1, 9))
+    else:
+        D, L, H, HS = (64 * int(rng.integers(1, n)) for n in (11, 9, 7, 5))
+    sn, rn = int(rng.integers(100, 161)), int(rng.integers(100, 161))
+    return replace(configs.get("mini_bf16"), name=f"random{i}", tokens=T, d_model=D, latent=L, n_experts=E,
+                   top_k=k, n_ranks=R, waves=W, expert_hidden=H, shared_experts=S, shared_hidden=HS,
+                   act="f32" if f32 else "bf16", send_num=sn, send_den=100, recv_num=rn, recv_den=100)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_all_ranks_random_shapes(runner, i):
+    """Every C-ABI call of the layer on a seeded random small shape (exact grid,
+    all ranks emulated), element by element against the oracle."""
+    sh = _random_shape(i)
+    gather = "buffer" if i % 4 == 3 else "fused"
+    _say(f"[all-ranks random] {sh.name} {sh.act} T={sh.tokens} D={sh.d_model} L={sh.latent} E={sh.n_experts} "
+         f"k={sh.top_k} R={sh.n_ranks} W={sh.waves} H={sh.expert_hidden} S={sh.shared_experts} "
+         f"HS={sh.shared_hidden} factors={sh.send_num}/{sh.recv_num} gather={gather}")
+    inp = gen.generate(sh, seed=20 + i, grid=True)
+    ref = O.layer_all_ranks(sh, inp)
+    lay = runner.AllRanksLayer(sh, inp, gather=gather)
+    lay.run()
+    torch.cuda.synchronize()
+    _check_all_ranks(sh, inp, ref, lay, True)
+
+
 def test_all_ranks_many_ranks(runner):
     """256 ranks of 2 experts, every one emulated: 257 send keys (9 key bits in
     the wave-ballot ranking instead of the 7 of 64 ranks) and a send cap of one
