@@ -430,7 +430,7 @@ class AllRanksLayer:
         bias = inp["bias"]
         if bias is not None and bias.ndim == 2:
             bias = np.broadcast_to(bias, (R,) + bias.shape)
-        self.bias = None if bias is None else upload(np.ascontiguousarray(bias, np.float32), dev)
+        self.bias = None if bias is None else upload_rank_blocks(np.ascontiguousarray(bias, np.float32), dev)
         self.bias_row_tokens = int(inp["bias_row_tokens"])
         self.w13 = upload(inp["w13"], dev)                              # [E][2H][L]
         self.w2 = upload(inp["w2"], dev)                                # [E][L][H]
@@ -531,7 +531,7 @@ class RaggedAllRanksLayer:
         bias = inp["bias"]
         if bias is not None and bias.ndim == 2:
             bias = np.broadcast_to(bias, (R,) + bias.shape)
-        self.bias = None if bias is None else upload(np.ascontiguousarray(bias, np.float32), dev)
+        self.bias = None if bias is None else upload_rank_blocks(np.ascontiguousarray(bias, np.float32), dev)
         self.bias_row_tokens = int(inp["bias_row_tokens"])
         self.w13 = upload(inp["w13"], dev)
         self.w2 = upload(inp["w2"], dev)

@@ -76,6 +76,11 @@ def assert_bar(gpu, ref_exact, act, what):
         return 0.0, 0.0
     rms = float(np.sqrt(np.mean(ref ** 2)))
     err = np.abs(gpu - ref)
+    if rms == 0.0:
+        # an all-zero exact output (every assignment of every token dropped and
+        # no shared experts): the bar has no scale, the result must be zero
+        assert not err.any(), f"{what}: exact output is all zero, the result is not (max |d| {err.max():.3g})"
+        return 0.0, 0.0
     beyond = np.maximum(err - 0.5 * ulp(ref, act), 0.0)
     ratio = float(beyond.max()) / rms
     raw = float(err.max()) / rms

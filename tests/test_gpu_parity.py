@@ -377,7 +377,8 @@ def _random_shape(i):
     """A small all-ranks shape drawn from a seeded generator: 2-8 ranks, 1-6
     local experts in 1-3 waves, top-1..6, up to 400 tokens, 0-2 shared experts,
     capacity factors 1.00-1.60, every width a multiple of 64 (bf16) or ragged
-    (float32, every third shape)."""
+    (float32, every third shape); no router bias, a Zipf-skewed bias or hot
+    experts per token segment in turn."""
     rng = np.random.default_rng(1000 + i)
     f32 = i % 3 == 2
     while True:
@@ -397,12 +398,17 @@ def _random_shape(i):
     else:
         D, L, H, HS = (64 * int(rng.integers(1, n)) for n in (11, 9, 7, 5))
     sn, rn = int(rng.integers(100, 161)), int(rng.integers(100, 161))
-    return replace(configs.get("mini_bf16"), name=f"random{i}", tokens=T, d_model=D, latent=L, n_experts=E,
-                   top_k=k, n_ranks=R, waves=W, expert_hidden=H, shared_experts=S, shared_hidden=HS,
-                   act="f32" if f32 else "bf16", send_num=sn, send_den=100, recv_num=rn, recv_den=100)
+    sh = replace(configs.get("mini_bf16"), name=f"random{i}", tokens=T, d_model=D, latent=L, n_experts=E,
+                 top_k=k, n_ranks=R, waves=W, expert_hidden=H, shared_experts=S, shared_hidden=HS,
+                 act="f32" if f32 else "bf16", send_num=sn, send_den=100, recv_num=rn, recv_den=100)
+    if i % 3 == 1:      # Zipf-skewed router bias
+        sh = replace(sh, bias="zipf", zipf_std=float(rng.uniform(0.5, 2.0)))
+    elif i % 3 == 2:    # hot experts per segment of tokens
+        sh = replace(sh, bias="segments", segment_tokens=int(rng.integers(10, 120)), segment_hot=max(1, E // 4))
+    return sh
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(24))
 def test_all_ranks_random_shapes(runner, i):
     """Every C-ABI call of the layer on a seeded random small shape (exact grid,
     all ranks emulated), element by element against the oracle."""
@@ -410,7 +416,7 @@ def test_all_ranks_random_shapes(runner, i):
     gather = "buffer" if i % 4 == 3 else "fused"
     _say(f"[all-ranks random] {sh.name} {sh.act} T={sh.tokens} D={sh.d_model} L={sh.latent} E={sh.n_experts} "
          f"k={sh.top_k} R={sh.n_ranks} W={sh.waves} H={sh.expert_hidden} S={sh.shared_experts} "
-         f"HS={sh.shared_hidden} factors={sh.send_num}/{sh.recv_num} gather={gather}")
+         f"HS={sh.shared_hidden} factors={sh.send_num}/{sh.recv_num} bias={sh.bias} gather={gather}")
     inp = gen.generate(sh, seed=20 + i, grid=True)
     ref = O.layer_all_ranks(sh, inp)
     lay = runner.AllRanksLayer(sh, inp, gather=gather)
