@@ -214,7 +214,19 @@ def test_all_ranks_ragged_dropless(runner, name, gather, banks):
     "ragged" lays each wave's hidden rows end to end in one bank as large as
     the rows the receiver's fullest wave keeps; "fixed" gives every expert a
     bank of the largest arrivals."""
-    base = _shape(name)
+    _ragged_dropless_case(runner, _shape(name), name, gather, banks)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_all_ranks_ragged_random_shapes(runner, i):
+    """The ragged dropless exchange on seeded random small shapes (the same
+    generator as test_all_ranks_random_shapes, other seeds), both bank modes."""
+    base = _random_shape(100 + i)
+    _ragged_dropless_case(runner, base, base.name, "buffer" if i % 3 == 0 else "fused",
+                          "ragged" if i % 2 else "fixed")
+
+
+def _ragged_dropless_case(runner, base, name, gather, banks):
     inp = gen.generate(base, seed=6, grid=True)
     pool_rows, expert_rows = _dropless_caps(base, inp)
     sh = configs.exact_fit(base, pool_rows, expert_rows)
