@@ -609,7 +609,23 @@ def _oracle_token_out(sh, inp, ref, tokens):
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
 def test_one_rank_full_size(runner, cfg):
-    sh = configs.get(cfg)
+    _one_rank_case(runner, configs.get(cfg), cfg)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_one_rank_random_shapes(runner, i):
+    """One rank's layer (the benchmark's class, two streams) on seeded random
+    small shapes: the other ranks' pools routed from their own tokens or drawn,
+    the full layer or dispatch only, the hot expert's rank as receiver under a
+    Zipf bias."""
+    sh = _random_shape(200 + i)
+    sh = replace(sh, name=f"onerank{i}", emulate_all_ranks=False, foreign=["routed", "drawn"][i % 2],
+                 receiver=["rank0", "hot_expert"][(i // 2) % 2] if sh.bias == "zipf" else "rank0",
+                 layer=["full", "full", "dispatch"][i % 3])
+    _one_rank_case(runner, sh, 10000 + i)
+
+
+def _one_rank_case(runner, sh, cfg):
     scap, rcap = O.capacities(sh)
     _say(f"[full-size] config {cfg} grid=True gather=fused")
     inp = gen.generate(sh, seed=0, grid=True, send_cap=scap)
@@ -671,7 +687,7 @@ def test_one_rank_full_size(runner, cfg):
         assert rep["send_dropped"] > 0  # segment-correlated routing overflows some pools
     # sampled float checks
     rng = np.random.default_rng(cfg)
-    tokens = np.unique(np.concatenate([[0, sh.tokens - 1], rng.choice(sh.tokens, 30, replace=False)]))
+    tokens = np.unique(np.concatenate([[0, sh.tokens - 1], rng.choice(sh.tokens, min(sh.tokens, 30), replace=False)]))
     z_ref = O.down_project(inp["x"][tokens], inp["w_down"], act)
     gz = host(lay.z[torch.as_tensor(tokens, device=lay.z.device)])
     assert np.array_equal(gz, z_ref), "z differs on the grid"
