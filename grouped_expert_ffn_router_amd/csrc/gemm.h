@@ -12,8 +12,11 @@
 // LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled per row,
 // so the fragment reads run at the bank-conflict-free rate.
 // The MFMA is issued with the B fragment as its first operand, so every lane
-// ends up holding one output row m and runs of 4 consecutive columns n: the
-// epilogue stores 8-byte pieces and resolves a row's destination once.
+// ends up holding one output row m and runs of 4 consecutive columns n.  The
+// bf16 store, scatter and SwiGLU epilogues (and the router's latent tiles)
+// round the tile into LDS and store whole row segments, 16 bytes per lane,
+// with each row's destination read when the tile starts; the router's logit
+// tiles and the tail-split fixup store a lane's 4-column pieces directly.
 // Workgroup ids are remapped so that each XCD (blocks are dealt round-robin
 // to the 8 XCDs) works on a contiguous, M-grouped range of tiles and reuses
 // operand rows from its own L2.
