@@ -1,10 +1,13 @@
 """Host-side checks of the C ABI (no GPU): symbols, capacities, validation."""
 
 import ctypes
+import math
 import re
 import os
+from fractions import Fraction
 
 import pytest
+from hypothesis import given, settings, strategies as st
 
 from grouped_expert_ffn_router_amd import binding as B
 from oracle import moe_oracle as O
@@ -193,3 +196,36 @@ def test_c_client_and_host_code_under_address_sanitizer(tmp_path):
     out = run([exe], env=env, timeout=120)
     assert out.startswith("ok"), out[-2000:]
     assert "ERROR: AddressSanitizer" not in out and "runtime error" not in out
+
+
+_FIELDS = [f for f, _ in B.Dims._fields_]
+_INT32 = st.one_of(st.integers(-3, 70000), st.sampled_from([-2**31, -1, 0, 1, 2**31 - 1, 2**30, 65536, 1 << 24]))
+
+
+@settings(max_examples=400, deadline=None, derandomize=True)
+@given(base=st.sampled_from([3, 5, "mini_bf16", "mini_f32"]),
+       edits=st.lists(st.tuples(st.sampled_from(_FIELDS), _INT32), min_size=1, max_size=3))
+def test_dims_fuzz_never_crashes_and_accepted_dims_are_consistent(base, edits):
+    """moe_capacity and moe_workspace_size on moe_dims with 1-3 fields set to
+    arbitrary int32 values (extremes included): each returns MOE_OK or a
+    documented error code, never crashes; when both accept the dims, the
+    capacities are the exact-rational closed forms and the workspace is
+    nonzero."""
+    d = B.make_dims(configs.get(base))
+    for f, v in edits:
+        setattr(d, f, v)
+    s, r, p = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = B.lib().moe_capacity(ctypes.byref(d), ctypes.byref(s), ctypes.byref(r), ctypes.byref(p))
+    b = ctypes.c_size_t()
+    rc2 = B.lib().moe_workspace_size(ctypes.byref(d), ctypes.byref(b))
+    codes = {B.MOE_OK, B.MOE_EINVAL, B.MOE_EDTYPE, B.MOE_EALIGN, B.MOE_ECAP}
+    assert rc in codes and rc2 in codes
+    if rc == B.MOE_OK:
+        T, k, R, E = d.tokens, d.top_k, d.n_ranks, d.n_experts
+        assert s.value == math.ceil(Fraction(d.send_num, d.send_den) * Fraction(T * k, R))
+        assert r.value == math.ceil(Fraction(d.recv_num, d.recv_den) * Fraction(R * T * k, E))
+        assert p.value > 0 and p.value % 16 == 0
+    if rc == B.MOE_OK and rc2 == B.MOE_OK:
+        assert b.value > 0
+    else:
+        assert B.last_error()
