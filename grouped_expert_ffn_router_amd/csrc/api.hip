@@ -179,13 +179,19 @@ int derive(const moe_dims* d, Q* q) {
   q->S = d->shared_experts; q->HS = d->shared_hidden; q->my_rank = d->my_rank; q->bf16 = bf16;
   q->esize = bf16 ? 2 : 4;
   const int64_t assign = q->T * q->k;
-  q->scap = ceil_div((int64_t)d->send_num * assign, (int64_t)d->send_den * q->R);
-  q->rcap = ceil_div((int64_t)d->recv_num * q->R * assign, (int64_t)d->recv_den * q->E);
-  q->row_bytes = q->L * q->esize;
-  q->prow = ceil_div(q->row_bytes + 4, 128) * 128;
-  if (assign > (1ll << 30) || q->R * q->scap > (1ll << 30) || q->WX * q->rcap > (1ll << 30) ||
+  // capacities in exact 128-bit arithmetic: the factors are any positive
+  // int32 rationals, so factor x load can exceed 64 bits before the range
+  // check below rejects it
+  const __int128 sd = (__int128)d->send_den * q->R, rd = (__int128)d->recv_den * q->E;
+  const __int128 scap = ((__int128)d->send_num * assign + sd - 1) / sd;
+  const __int128 rcap = ((__int128)d->recv_num * q->R * assign + rd - 1) / rd;
+  if (assign > (1ll << 30) || scap * q->R > (1ll << 30) || rcap * q->WX > (1ll << 30) ||
       q->T * q->E > (1ll << 31) || q->T * q->D > (1ll << 40))
     return fail(MOE_EINVAL, "sizes exceed the 32-bit index range of the kernels");
+  q->scap = (int64_t)scap;
+  q->rcap = (int64_t)rcap;
+  q->row_bytes = q->L * q->esize;
+  q->prow = ceil_div(q->row_bytes + 4, 128) * 128;
   return MOE_OK;
 }
 

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <stdint.h>
+
 #include "moe.h"
 
 static int fail(const char* what) {
@@ -62,6 +64,41 @@ int main(void) {
   if (moe_route(&d, NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL) != MOE_EINVAL)
     return fail("NULL input accepted");
   if (strstr(moe_last_error(), "NULL") == NULL) return fail("error message");
+
+  /* dims fuzz: 1-3 fields of the layer above set to arbitrary int32 values
+     (extremes included) from a fixed linear congruential sequence; the host
+     code must answer with a documented code every time (and, under the
+     sanitizers, without undefined behaviour such as a signed overflow) */
+  {
+    static const int32_t special[] = {INT32_MIN, -1, 0, 1, 2, 3, 7, 63, 64, 100, 1000, 4096, 65536,
+                                      1 << 24, 1 << 30, INT32_MAX};
+    const int nspecial = (int)(sizeof(special) / sizeof(special[0]));
+    uint64_t lcg = 0x9e3779b97f4a7c15ull;
+    int accepted = 0;
+    for (int it = 0; it < 20000; ++it) {
+      moe_dims f = d;
+      int32_t* fields = (int32_t*)&f;
+      const int nfields = (int)(sizeof(moe_dims) / sizeof(int32_t));
+      lcg = lcg * 6364136223846793005ull + 1442695040888963407ull;
+      const int nedit = 1 + (int)((lcg >> 60) % 3);
+      for (int e = 0; e < nedit; ++e) {
+        lcg = lcg * 6364136223846793005ull + 1442695040888963407ull;
+        const int field = (int)((lcg >> 33) % (uint64_t)nfields);
+        const int32_t v = (lcg >> 62) ? special[(lcg >> 40) % (uint64_t)nspecial] : (int32_t)((lcg >> 20) % 70000) - 3;
+        fields[field] = v;
+      }
+      int64_t s = 0, r = 0, p = 0;
+      size_t b = 0;
+      const int rc = moe_capacity(&f, &s, &r, &p), rc2 = moe_workspace_size(&f, &b);
+      if (rc != MOE_OK && rc != MOE_EINVAL && rc != MOE_EDTYPE) return fail("fuzz: moe_capacity code");
+      if (rc2 != MOE_OK && rc2 != MOE_EINVAL && rc2 != MOE_EDTYPE) return fail("fuzz: moe_workspace_size code");
+      if (rc == MOE_OK && (s <= 0 || r <= 0 || p <= 0 || p % 16)) {
+        if (!(s == 0 && f.tokens == 0)) return fail("fuzz: accepted dims gave bad capacities");
+      }
+      if (rc == MOE_OK && rc2 == MOE_OK) ++accepted;
+    }
+    if (accepted == 0) return fail("fuzz: nothing accepted");
+  }
   printf("ok send_cap=%lld recv_cap=%lld stride=%lld workspace=%zu\n", (long long)send_cap, (long long)recv_cap,
          (long long)stride, ws);
   return 0;
