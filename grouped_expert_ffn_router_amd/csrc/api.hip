@@ -161,12 +161,12 @@ int derive(const moe_dims* d, Q* q) {
     return fail(MOE_EINVAL, "live_waves %d out of range [0, waves = %d]", d->live_waves, d->waves);
   if (d->wave_rows < 0) return fail(MOE_EINVAL, "wave_rows %d < 0", d->wave_rows);
   const bool bf16 = d->act_dtype == MOE_ACT_BF16;
+  // the up-projection GEMM's K (latent plus the shared hidden units) picks its segment in float
+  if ((int64_t)d->latent + (int64_t)d->shared_experts * d->shared_hidden >= (1ll << 24))
+    return fail(MOE_EINVAL, "latent + shared_experts * shared_hidden must be below 2^24");
   if (bf16) {
     if (d->d_model % 64 || d->latent % 64 || d->expert_hidden % 64 || d->shared_hidden % 64)
       return fail(MOE_EINVAL, "bf16 layers need d_model, latent, expert_hidden, shared_hidden multiples of 64");
-    // the up-projection GEMM's K (latent plus the shared hidden units) picks its segment in float
-    if ((int64_t)d->latent + (int64_t)d->shared_experts * d->shared_hidden >= (1ll << 24))
-      return fail(MOE_EINVAL, "latent + shared_experts * shared_hidden must be below 2^24");
     if (d->n_experts % 4) return fail(MOE_EINVAL, "bf16 layers need n_experts to be a multiple of 4");
   } else if (d->latent % 8 || d->shared_hidden % 4) {
     // the combined [latent | shared hidden] rows are written with 16-byte stores
@@ -190,6 +190,17 @@ int derive(const moe_dims* d, Q* q) {
     return fail(MOE_EINVAL, "sizes exceed the 32-bit index range of the kernels");
   q->scap = (int64_t)scap;
   q->rcap = (int64_t)rcap;
+  // widths and GEMM tile counts the kernels' 32-bit tile and column
+  // arithmetic can hold (far beyond any layer's shape)
+  if (q->D > (1 << 24) || q->L > (1 << 24) || q->H > (1 << 24) || q->HS > (1 << 24))
+    return fail(MOE_EINVAL, "d_model, latent, expert_hidden and shared_hidden must be at most 2^24");
+  auto tiles = [](int64_t groups, int64_t rows, int64_t cols) {
+    return groups * ceil_div(rows, 256) * ceil_div(cols, 256);
+  };
+  if (tiles(1, q->T, q->E + q->L) > (1ll << 30) || tiles(1, q->T, 2 * q->S * q->HS) > (1ll << 30) ||
+      tiles(q->WX, q->rcap, 2 * q->H) > (1ll << 30) || tiles(q->WX, q->rcap, q->L) > (1ll << 30) ||
+      tiles(1, q->T, q->D) > (1ll << 30))
+    return fail(MOE_EINVAL, "a GEMM of these dims has more output tiles than the kernels can count");
   q->row_bytes = q->L * q->esize;
   q->prow = ceil_div(q->row_bytes + 4, 128) * 128;
   return MOE_OK;

@@ -95,6 +95,8 @@ int main(void) {
       if (rc == MOE_OK && (s <= 0 || r <= 0 || p <= 0 || p % 16)) {
         if (!(s == 0 && f.tokens == 0)) return fail("fuzz: accepted dims gave bad capacities");
       }
+      /* no wrapped size: the workspace holds at least the 4-byte send rank of every assignment */
+      if (rc2 == MOE_OK && b < (size_t)f.tokens * (size_t)f.top_k * 4u) return fail("fuzz: workspace size wrapped");
       if (rc == MOE_OK && rc2 == MOE_OK) ++accepted;
     }
     if (accepted == 0) return fail("fuzz: nothing accepted");
