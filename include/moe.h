@@ -68,7 +68,16 @@ enum { MOE_ACT_BF16 = 0, MOE_ACT_F32 = 1 };
  * X = E / R local experts per rank, W waves (X / W experts per wave), H routed
  * expert hidden width, S shared experts, HS shared hidden width.  Capacity
  * factors are rationals: send = send_num / send_den (1.10 = 110/100), receive
- * = recv_num / recv_den (1.15 = 115/100). */
+ * = recv_num / recv_den (1.15 = 115/100).
+ *
+ * Accepted dims (every entry point returns MOE_EINVAL otherwise, MOE_EDTYPE
+ * for an unknown act_dtype): T >= 0, S >= 0, every other size positive;
+ * E a multiple of R with X <= MOE_MAX_LOCAL and X a multiple of W;
+ * R <= MOE_MAX_RANKS; k <= min(32, E); E <= 2048; 0 <= my_rank < R; positive
+ * capacity factors; D, L, H, HS <= 2^24 and L + S * HS < 2^24; bf16: D, L, H,
+ * HS multiples of 64 and E a multiple of 4; fp32: L a multiple of 8 and HS of
+ * 4; T * k, R * send_cap and X/W * recv_cap at most 2^30, T * E at most 2^31,
+ * and each GEMM at most 2^30 output tiles of 256 x 256. */
 typedef struct moe_dims {
   int32_t tokens, d_model, latent, n_experts, top_k, n_ranks, waves;
   int32_t expert_hidden, shared_experts, shared_hidden;
