@@ -229,3 +229,33 @@ def test_dims_fuzz_never_crashes_and_accepted_dims_are_consistent(base, edits):
         assert b.value > 0
     else:
         assert B.last_error()
+
+
+def test_host_entry_points_from_many_threads():
+    """Eight host threads call moe_capacity / moe_workspace_size at once, half
+    with valid dims and half with dims the library rejects: every thread gets
+    its own results and its own error message (the message is thread-local)."""
+    import threading
+    good = B.make_dims(configs.get(3))
+    want = B.capacity(good), B.workspace_size(good)
+    errors = []
+
+    def worker(i):
+        try:
+            for _ in range(2000):
+                if i % 2:
+                    assert (B.capacity(good), B.workspace_size(good)) == want
+                else:
+                    d = B.make_dims(configs.get(3))
+                    d.waves = (4, 5, 7, 8)[i // 2]   # 6 local experts in 4, 5, 7 or 8 waves
+                    rc = B.lib().moe_capacity(ctypes.byref(d), None, None, None)
+                    assert rc == B.MOE_EINVAL and b"waves" in B.lib().moe_last_error()
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
