@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -83,9 +84,9 @@ LaunchEvents& launch_events() {
 
 namespace {
 
-class KernelTimer {  // scope guard around one launch
+class KernelTimer {  // scope guard around one launch (whose dispatch records the events on its own stream)
  public:
-  KernelTimer(const char* name, hipStream_t st) : st_(st) {
+  explicit KernelTimer(const char* name) {
     Timing& t = timing();
     std::lock_guard<std::mutex> g(t.mu);
     if (!t.on) return;
@@ -116,17 +117,16 @@ class KernelTimer {  // scope guard around one launch
   }
 
  private:
-  hipStream_t st_;
   TimingRec rec_{};
   bool armed_ = false;
 };
 
 // Launch `expr` (a hipError_t expression) timed under `name`.
-#define LAUNCH(name, st, expr, where)          \
+#define LAUNCH(name, expr, where)              \
   do {                                         \
     hipError_t e_;                             \
     {                                          \
-      KernelTimer kt_(name, st);               \
+      KernelTimer kt_(name);                   \
       e_ = (expr);                             \
     }                                          \
     if (e_ != hipSuccess) return hip_fail(e_, where); \
@@ -274,15 +274,15 @@ P* at(void* ws, size_t off) { return (P*)((char*)ws + off); }
 
 // Compute units of the current device (cached per device).
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];  // 0: not looked up yet (threads may race to fill it, with one value)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PART_SLOTS;
-  if (!cached[dev]) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (!n) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = PART_SLOTS;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // bf16 GEMM launch.  part: PART_SLOTS partial tiles for the tail split, or
@@ -307,14 +307,14 @@ hipError_t gemm_bf16(const char* name, const char* fixup_name, A a, B b, E e, in
     split = r > 0 && 2 * r <= P && parts >= 2 && nk - nk / parts >= KSPLIT_GAIN;
   }
   {
-    KernelTimer kt(name, st);
+    KernelTimer kt(name);
     launch((gemm_bf16_mfma<Cfg, GATEUP, A, B, E>), dim3((unsigned)gemm_grid(max_tiles, P)), dim3(Cfg::NT), 0,
                        st, a, b, e, N, K, groups, (int)tiles_n, P, split ? part : nullptr);
     hipError_t r = hipGetLastError();
     if (r != hipSuccess) return r;
   }
   if (!split) return hipSuccess;
-  KernelTimer kt(fixup_name, st);
+  KernelTimer kt(fixup_name);
   launch((gemm_bf16_fixup<Cfg, GATEUP, A, E>), dim3(2048u), dim3(64), 0, st, a, e,
                      N, K, groups, (int)tiles_n, P, (const float*)part);
   return hipGetLastError();
@@ -324,7 +324,7 @@ template <bool GATEUP, class A, class B, class E>
 hipError_t gemm_f32(const char* name, A a, B b, E e, int N, int K, int64_t max_rows, int groups, hipStream_t st) {
   const int cols = GATEUP ? N / 2 : N;
   if (cols <= 0 || max_rows <= 0 || groups <= 0) return hipSuccess;
-  KernelTimer kt(name, st);
+  KernelTimer kt(name);
   const dim3 grid((unsigned)ceil_div(cols, 16), (unsigned)ceil_div(max_rows, 16), (unsigned)groups);
   launch((gemm_f32_simple<GATEUP, A, B, E>), grid, dim3(16, 16), 0, st, a, b, e, N, K);
   return hipGetLastError();
@@ -410,11 +410,11 @@ int check_pack_args(const Q& q, const void* z, const int32_t* topk_idx, const vo
 int pack_pools_run(const Q& q, const void* z, const int32_t* topk_idx, void* send_pools, int64_t dst_stride_bytes,
                    int32_t* slot_of, int32_t* send_count, int32_t* ctr, int32_t* s_cc, int32_t* s_cb,
                    int32_t* s_lr, int nch_s, hipStream_t st) {
-  LAUNCH("send_rank", st, launch_send_rank(topk_idx, (int)(q.T * q.k), (int)q.X, (int)q.E, (int)q.R, s_lr, s_cc, st),
+  LAUNCH("send_rank", launch_send_rank(topk_idx, (int)(q.T * q.k), (int)q.X, (int)q.E, (int)q.R, s_lr, s_cc, st),
          "moe_pack_pools rank");
-  LAUNCH("send_scan", st, launch_send_scan(s_cc, nch_s, (int)q.R, (int)q.scap, s_cb, ctr, send_count, st),
+  LAUNCH("send_scan", launch_send_scan(s_cc, nch_s, (int)q.R, (int)q.scap, s_cb, ctr, send_count, st),
          "moe_pack_pools scan");
-  LAUNCH("pack", st, launch_pack(z, q.row_bytes, topk_idx, s_lr, s_cb, (int)q.T, (int)q.k, (int)q.X, (int)q.E,
+  LAUNCH("pack", launch_pack(z, q.row_bytes, topk_idx, s_lr, s_cb, (int)q.T, (int)q.k, (int)q.X, (int)q.E,
                                  (int)q.R, (int)q.scap, send_pools, dst_stride_bytes, q.prow, slot_of, send_count,
                                  nullptr, ctr, st),
          "moe_pack_pools pack");
@@ -568,7 +568,7 @@ int moe_route(const moe_dims* dims, const void* x, const void* w_router, const v
   HIP_TRY(q.bf16 ? route_gemm<bf16_t>(q, x, w_router, w_down, bias, bias_row_tokens, lg, z, at<float>(ws, w.part), st)
                  : route_gemm<float>(q, x, w_router, w_down, bias, bias_row_tokens, lg, z, nullptr, st),
           "moe_route gemm");
-  LAUNCH("select_topk", st, launch_select_topk(lg, (int)q.T, (int)q.E, (int)q.k, topk_idx, topk_w, st), "moe_route select");
+  LAUNCH("select_topk", launch_select_topk(lg, (int)q.T, (int)q.E, (int)q.k, topk_idx, topk_w, st), "moe_route select");
   return MOE_OK;
 }
 
@@ -615,12 +615,12 @@ int moe_pack_ragged(const moe_dims* dims, const void* z, const int32_t* topk_idx
   hipStream_t st = (hipStream_t)stream;
   int32_t* ctr = at<int32_t>(ws, w.ctr);
   const int no_cap = INT32_MAX;
-  LAUNCH("send_rank", st, launch_send_rank(topk_idx, (int)(q.T * q.k), (int)q.X, (int)q.E, (int)q.R, at<int32_t>(ws, w.s_lr),
+  LAUNCH("send_rank", launch_send_rank(topk_idx, (int)(q.T * q.k), (int)q.X, (int)q.E, (int)q.R, at<int32_t>(ws, w.s_lr),
                            at<int32_t>(ws, w.s_cc), st), "moe_pack_ragged rank");
-  LAUNCH("send_scan", st, launch_send_scan(at<int32_t>(ws, w.s_cc), w.nch_s, (int)q.R, no_cap, at<int32_t>(ws, w.s_cb), ctr,
+  LAUNCH("send_scan", launch_send_scan(at<int32_t>(ws, w.s_cc), w.nch_s, (int)q.R, no_cap, at<int32_t>(ws, w.s_cb), ctr,
                            send_count, st), "moe_pack_ragged scan");
-  LAUNCH("ragged_offsets", st, launch_ragged_offsets(send_count, (int)q.R, send_off, st), "moe_pack_ragged offsets");
-  LAUNCH("pack", st, launch_pack(z, q.row_bytes, topk_idx, at<int32_t>(ws, w.s_lr), at<int32_t>(ws, w.s_cb), (int)q.T,
+  LAUNCH("ragged_offsets", launch_ragged_offsets(send_count, (int)q.R, send_off, st), "moe_pack_ragged offsets");
+  LAUNCH("pack", launch_pack(z, q.row_bytes, topk_idx, at<int32_t>(ws, w.s_lr), at<int32_t>(ws, w.s_cb), (int)q.T,
                       (int)q.k, (int)q.X, (int)q.E, (int)q.R, no_cap, send_rows, 0, q.prow, slot_of, send_count,
                       send_off, ctr, st), "moe_pack_ragged pack");
   return MOE_OK;
@@ -639,12 +639,12 @@ int moe_recv_rank(const moe_dims* dims, const void* recv_pools, int64_t src_stri
   const int n_rows = (int)(q.R * q.scap);
   int32_t* arrivals = ctr + Ctr::HEADER + 2 * q.R;
   int32_t* kept = arrivals + q.X;
-  LAUNCH("recv_rank", st, launch_recv_rank(recv_pools, src_stride_bytes, q.prow, q.row_bytes, (int)q.R, (int)q.scap, (int)q.X,
+  LAUNCH("recv_rank", launch_recv_rank(recv_pools, src_stride_bytes, q.prow, q.row_bytes, (int)q.R, (int)q.scap, (int)q.X,
                            (int)q.my_rank, at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cc),
                            st), "moe_recv_rank rank");
-  LAUNCH("recv_scan", st, launch_recv_scan(at<int32_t>(ws, w.r_cc), w.nch_r, (int)q.X, (int)q.rcap, at<int32_t>(ws, w.r_cb),
+  LAUNCH("recv_scan", launch_recv_scan(at<int32_t>(ws, w.r_cc), w.nch_r, (int)q.X, (int)q.rcap, at<int32_t>(ws, w.r_cb),
                            arrivals, kept, ctr, st), "moe_recv_rank scan");
-  LAUNCH("recv_final", st, launch_recv_final(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cb), n_rows,
+  LAUNCH("recv_final", launch_recv_final(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_lr), at<int32_t>(ws, w.r_cb), n_rows,
                             (int)q.X, at<int32_t>(ws, w.r_rank), st), "moe_recv_rank final");
   return MOE_OK;
 }
@@ -667,10 +667,10 @@ int moe_recv_waves(const moe_dims* dims, const void* recv_pools, int64_t src_str
   int32_t* ctr = at<int32_t>(ws, w.ctr);
   const int j0 = wave * (int)q.WX, nj = (int)q.WX, n_rows = (int)(q.R * q.scap);
   const int32_t* kept = ctr + Ctr::HEADER + 2 * q.R + q.X;
-  LAUNCH("recv_place", st, launch_recv_place(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_rank), kept, n_rows, (int)q.rcap, j0,
+  LAUNCH("recv_place", launch_recv_place(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_rank), kept, n_rows, (int)q.rcap, j0,
                             nj, q.WR, wave_count, row_src, ctr, st), "moe_recv_waves place");
   if (wave_buf)
-    LAUNCH("wave_gather", st, launch_wave_gather(recv_pools, src_stride_bytes, q.prow, (int)q.scap, q.row_bytes, row_src, wave_count,
+    LAUNCH("wave_gather", launch_wave_gather(recv_pools, src_stride_bytes, q.prow, (int)q.scap, q.row_bytes, row_src, wave_count,
                                nj, (int)q.rcap, wave_buf, st), "moe_recv_waves gather");
   return MOE_OK;
 }
@@ -720,7 +720,7 @@ int moe_expert_gemm(const moe_dims* dims, int32_t wave, const void* wave_buf, co
     }
   }
   HIP_TRY(r, "moe_expert_gemm gemm");
-  LAUNCH("zero_dropped", st, launch_zero_dropped(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_rank), (int)(q.R * q.scap), (int)q.scap,
+  LAUNCH("zero_dropped", launch_zero_dropped(at<int32_t>(ws, w.r_j), at<int32_t>(ws, w.r_rank), (int)(q.R * q.scap), (int)q.scap,
                               (int)q.rcap, wave * (int)q.WX, (int)q.WX, ret_pools, ret_src_stride_bytes, q.row_bytes,
                               st), "moe_expert_gemm zero rows");
   return MOE_OK;
@@ -755,7 +755,7 @@ int moe_combine(const moe_dims* dims, const void* ret_pools, int64_t ret_dst_str
   hipStream_t st = (hipStream_t)stream;
   void* cat = at<char>(ws, w.cat);
   const int64_t ldc = q.L + q.S * q.HS;
-  LAUNCH("combine", st, launch_combine(q.bf16 ? 0 : 1, ret_pools, ret_dst_stride_bytes, q.row_bytes, (int)q.scap,
+  LAUNCH("combine", launch_combine(q.bf16 ? 0 : 1, ret_pools, ret_dst_stride_bytes, q.row_bytes, (int)q.scap,
                                        (int)q.R, slot_of, topk_w, (int)q.T, (int)q.k, (int)q.L, cat, ldc,
                                        at<int32_t>(ws, w.ctr), st),
          "moe_combine combine");
