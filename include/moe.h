@@ -29,7 +29,8 @@
  *     order on one stream, except: moe_shared_experts touches only its own
  *     region and may run beside the routed calls, and after moe_recv_rank the
  *     calls of waves in different scratch blocks (dims.live_waves) may run
- *     side by side.
+ *     side by side.  Layers with their own workspaces and buffers may be
+ *     driven from different host threads and streams at the same time.
  *   - Activations and weights are bf16 (act_dtype 0) or fp32 (act_dtype 1);
  *     accumulation is fp32; logits and routing weights are fp32.
  *   - Return 0 (MOE_OK) or a negative MOE_E* code; moe_last_error() returns a

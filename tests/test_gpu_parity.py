@@ -995,6 +995,82 @@ def test_graph_replay_same_bits(runner):
     torch.cuda.empty_cache()
 
 
+def test_two_host_threads_same_bits(runner):
+    """Two independent layers (own inputs, workspaces and streams) driven from
+    two host threads at once, with kernel timing on, give the bits each gives
+    alone, and every launch of both threads is timed: the library keeps no
+    state between calls outside the workspace except the thread-local error
+    message and the timing's per-thread launch events."""
+    import threading
+    from concurrent.futures import ThreadPoolExecutor
+    from grouped_expert_ffn_router_amd import binding as B
+    sh = replace(configs.get(3), tokens=2048)
+    scap, _ = O.capacities(sh)
+    _say("[two threads] config 3 shape at 2048 tokens per rank, seeds 6 and 7, three steps per thread")
+    lays = []
+    for seed in (6, 7):
+        inp = gen.generate(sh, seed=seed, send_cap=scap)
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            drawn = dict(zip(range(sh.n_ranks), ex.map(inp["sources"], range(sh.n_ranks))))
+        inp["sources"] = drawn.__getitem__
+        lays.append(runner.OneRankLayer(sh, inp, gather="fused", live_waves=2))
+    names = ("out", "z", "logits", "ret_send", "slot_of", "row_src", "wave_count")
+    streams = [(torch.cuda.Stream(), torch.cuda.Stream()) for _ in lays]
+
+    def snapshot(lay):
+        return [host(getattr(lay, n)).view(np.uint8).copy() for n in names]
+
+    want = []
+    for lay, (main, side) in zip(lays, streams):
+        for _ in range(2):
+            lay.run(main, side)
+        torch.cuda.synchronize()
+        want.append(snapshot(lay))
+    assert not np.array_equal(want[0][0], want[1][0]), "the two layers must give different outputs"
+    for lay in lays:
+        for n in ("out", "z", "logits", "ret_send"):
+            getattr(lay, n).zero_()
+    torch.cuda.synchronize()
+
+    steps, errors = 3, []
+    start = threading.Barrier(2)
+
+    def drive(i):
+        try:
+            main, side = streams[i]
+            start.wait(timeout=60)
+            for _ in range(steps):
+                lays[i].run(main, side)
+            main.synchronize()
+            side.synchronize()
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(e)
+
+    B.timing_read()  # drop earlier records
+    B.timing_enable(True)
+    try:
+        threads = [threading.Thread(target=drive, args=(i,)) for i in range(2)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join(timeout=120)
+        assert not any(t.is_alive() for t in threads), "a driver thread did not finish"
+        torch.cuda.synchronize()
+        timed = B.timing_read()
+    finally:
+        B.timing_enable(False)
+    assert not errors, errors
+    for i, lay in enumerate(lays):
+        for a, b, n in zip(snapshot(lay), want[i], names):
+            assert np.array_equal(a, b), f"layer {i}: {n} differs when run beside the other thread"
+    per_step = {"route_gemm": 1, "pack": 1, "combine": 1, "shared_gate_up": 1, "up_shared_down": 1,
+                "expert_gate_up": sh.waves, "expert_down": sh.waves}
+    for name, n in per_step.items():
+        assert timed[name][0] == 2 * steps * n, (name, timed[name])
+    del lays
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_one_rank_ragged_full_size(runner, cfg):
     """The ragged dropless layer at one rank's real shape against the fixed-pool
