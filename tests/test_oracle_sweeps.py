@@ -11,7 +11,9 @@ from the rule itself, not from the oracle's vectorised code:
     destination;
   * receive slots (one fixed row block per local expert, capped): a row's
     rank is the number of earlier (source, slot) rows of the same expert;
-  * capacities: the ceiling of factor x balanced load, in exact rationals.
+  * capacities: the ceiling of factor x balanced load, in exact rationals;
+  * whole layers on tiny shapes: every token against the dense MoE formula
+    with the assignments that survive both caps (found by enumeration).
 """
 
 from fractions import Fraction
@@ -126,3 +128,94 @@ def test_capacities_sweep(T, k, R, Xr, num, den):
     E = R * Xr
     assert O.send_capacity(T, k, R, num, den) == math.ceil(Fraction(num, den) * Fraction(T * k, R))
     assert O.recv_capacity(T, k, R, E, num, den) == math.ceil(Fraction(num, den) * Fraction(R * T * k, E))
+
+
+def _sweep_shape(R, X, W, k, T, S, sn, rn):
+    from dataclasses import replace
+    from workload import configs
+    return replace(configs.get("mini_f32"), name="sweep", tokens=T, d_model=6, latent=8, n_experts=R * X, top_k=k,
+                   n_ranks=R, waves=W, expert_hidden=4, shared_experts=S, shared_hidden=4,
+                   send_num=sn, send_den=100, recv_num=rn, recv_den=100)
+
+
+@settings(max_examples=60, deadline=None, derandomize=True)
+@given(st.data())
+def test_layer_sweep_against_textbook_tokens(data):
+    """Whole oracle layers on tiny random shapes (ranks, experts per rank,
+    waves, top-k, shared experts, both capacity factors), every token of
+    every rank against the dense MoE formula written out per token: the
+    routed terms that survive both caps, found by enumeration, weights not
+    renormalised, plus the shared path ([P1] sections 二 and 四).  The drop
+    ledger equals the enumerated counts."""
+    from test_oracle_pins import _brute_kept, _textbook_token
+    from workload import gen
+    R = data.draw(st.integers(1, 4), label="R")
+    X = data.draw(st.integers(1, 3), label="X")
+    E = R * X
+    W = data.draw(st.sampled_from([w for w in range(1, X + 1) if X % w == 0]), label="waves")
+    k = data.draw(st.integers(1, min(4, E)), label="k")
+    T = data.draw(st.integers(1, 10), label="T")
+    S = data.draw(st.integers(0, 2), label="S")
+    sn = data.draw(st.integers(20, 150), label="send %")
+    rn = data.draw(st.integers(20, 150), label="recv %")
+    sh = _sweep_shape(R, X, W, k, T, S, sn, rn)
+    inp = gen.generate(sh, seed=data.draw(st.integers(0, 10**6), label="seed"))
+    res = O.layer_all_ranks(sh, inp)
+    idx = [res["dispatch"][s]["idx"] for s in range(R)]
+    send_kept, recv_kept = _brute_kept(idx, X, R, res["send_cap"], res["recv_cap"])
+    for s in range(R):
+        d = res["dispatch"][s]
+        for t in range(T):
+            ref = _textbook_token(sh, inp, s, t, d["idx"][t], d["w"][t], kept=recv_kept[s, t])
+            np.testing.assert_allclose(res["out"][s]["out_exact"][t], ref, rtol=1e-9, atol=1e-12)
+    assert int(res["ledger"]["send_dropped"].sum()) == int((~send_kept).sum())
+    assert int(res["ledger"]["recv_dropped"].sum()) == int((send_kept & ~recv_kept).sum())
+    assert res["ledger"]["kept"] == int(recv_kept.sum()) and res["ledger"]["total"] == R * T * k
+
+
+def test_layer_with_an_empty_batch():
+    """T = 0 on every rank: empty outputs, nothing kept or dropped."""
+    from workload import gen
+    sh = _sweep_shape(3, 2, 2, 2, 0, 1, 110, 115)
+    res = O.layer_all_ranks(sh, gen.generate(sh, seed=3))
+    assert all(res["out"][s]["out_exact"].shape == (0, sh.d_model) for s in range(sh.n_ranks))
+    assert res["ledger"]["kept"] == 0 and res["ledger"]["total"] == 0
+    assert not res["ledger"]["send_dropped"].any() and not res["ledger"]["recv_dropped"].any()
+
+
+def test_layer_sweep_catches_planted_mistakes(monkeypatch):
+    """Each mistake planted in the oracle makes the layer sweep fail."""
+    good_send, good_recv, good_ret, good_comb = O.send_slots, O.recv_slots, O.expert_returns, O.combine
+
+    def send_kslot_major(idx, X, R, cap):  # ranks in (k-slot, token) order
+        r = good_send(np.ascontiguousarray(idx.T), X, R, cap)
+        return dict(r, slot_of=np.ascontiguousarray(r["slot_of"].T))
+
+    def recv_slot_major(pool_ids, my_rank, X, recv_cap):  # rows visited slot by slot across sources
+        r = good_recv(np.ascontiguousarray(pool_ids.T), my_rank, X, recv_cap)
+        n_src, cap = pool_ids.shape
+        pos = r["row_src"]
+        src_of = np.where(pos >= 0, (pos % n_src) * cap + pos // n_src, -1)
+        return dict(r, row_src=src_of, row_rank=r["row_rank"].T, row_expert=r["row_expert"].T)
+
+    def leaky_returns(pool_rows, recv, w13, w2, hidden, act):  # rows past recv_cap return expert outputs
+        X = len(recv["count"])
+        je, rk = recv["row_expert"].reshape(-1), recv["row_rank"].reshape(-1)
+        row_src = np.full((X, max(int(recv["arrivals"].max()), 1)), -1, dtype=np.int64)
+        for j in range(X):
+            pos = np.flatnonzero(je == j)
+            row_src[j, rk[pos]] = pos
+        return good_ret(pool_rows, dict(recv, count=recv["arrivals"], row_src=row_src), w13, w2, hidden, act)
+
+    def renormalised(ret, slot_of, w, cap, act):  # weights renormalised over the assignments kept at send
+        kept = np.where(slot_of >= 0, w, 0.0)
+        sums = kept.sum(axis=1, keepdims=True)
+        return good_comb(ret, slot_of, np.where(sums > 0, kept / np.where(sums > 0, sums, 1), 0.0), cap, act)
+
+    for name, fn in (("send_slots", send_kslot_major), ("recv_slots", recv_slot_major),
+                     ("expert_returns", leaky_returns), ("combine", renormalised)):
+        monkeypatch.setattr(O, name, fn)
+        with pytest.raises(AssertionError):
+            test_layer_sweep_against_textbook_tokens()
+        monkeypatch.undo()
+    test_layer_sweep_against_textbook_tokens()  # and passes again
