@@ -130,19 +130,20 @@ def test_capacities_sweep(T, k, R, Xr, num, den):
     assert O.recv_capacity(T, k, R, E, num, den) == math.ceil(Fraction(num, den) * Fraction(R * T * k, E))
 
 
-def _sweep_shape(R, X, W, k, T, S, sn, rn):
+def _sweep_shape(R, X, W, k, T, S, sn, rn, act="f32"):
     from dataclasses import replace
     from workload import configs
     return replace(configs.get("mini_f32"), name="sweep", tokens=T, d_model=6, latent=8, n_experts=R * X, top_k=k,
                    n_ranks=R, waves=W, expert_hidden=4, shared_experts=S, shared_hidden=4,
-                   send_num=sn, send_den=100, recv_num=rn, recv_den=100)
+                   send_num=sn, send_den=100, recv_num=rn, recv_den=100, act=act)
 
 
 @settings(max_examples=60, deadline=None, derandomize=True)
 @given(st.data())
 def test_layer_sweep_against_textbook_tokens(data):
     """Whole oracle layers on tiny random shapes (ranks, experts per rank,
-    waves, top-k, shared experts, both capacity factors), every token of
+    waves, top-k, shared experts, both capacity factors; fp32 or bf16
+    activations with their rounding points), every token of
     every rank against the dense MoE formula written out per token: the
     routed terms that survive both caps, found by enumeration, weights not
     renormalised, plus the shared path ([P1] sections 二 and 四).  The drop
@@ -158,7 +159,8 @@ def test_layer_sweep_against_textbook_tokens(data):
     S = data.draw(st.integers(0, 2), label="S")
     sn = data.draw(st.integers(20, 150), label="send %")
     rn = data.draw(st.integers(20, 150), label="recv %")
-    sh = _sweep_shape(R, X, W, k, T, S, sn, rn)
+    act = data.draw(st.sampled_from(["f32", "bf16"]), label="act")
+    sh = _sweep_shape(R, X, W, k, T, S, sn, rn, act)
     inp = gen.generate(sh, seed=data.draw(st.integers(0, 10**6), label="seed"))
     res = O.layer_all_ranks(sh, inp)
     idx = [res["dispatch"][s]["idx"] for s in range(R)]
