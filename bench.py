@@ -23,6 +23,7 @@ Options: --steps K --warmup W --config {2,3,4,5,6} --gather {fused,buffer} --str
 --sweep-capacity (one line per capacity-factor point instead of the benchmark line),
 --dropless (capacities fitted to the exchanged counts against the fixed factors),
 --vendor-gemm (torch's bf16 matmul on the layer's GEMM shapes, a reference point for the GEMM core)
+--graph (the step captured once as a HIP graph, its replays timed)
 --no-cpu-baseline --cpu-tokens N --seed S.  --gpus N > 1 exits: the benchmark
 measures one GPU.
 """
@@ -63,6 +64,8 @@ def parse():
                     help="waves whose scratch (SwiGLU hidden rows, partial tiles) the workspace holds at once; "
                          "2 (default): two waves overlap, one on each stream, as many as two streams can run; "
                          "1: one wave live at a time, waves in order; 0: all waves")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (both streams) as a HIP graph after the warm-up and time its replays")
     ap.add_argument("--cpu-runs", type=int, default=0,
                     help="timed runs of the CPU oracle (the median is reported); 0: 3, or 1 for 65,536 tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -429,6 +432,26 @@ def main():
     for _ in range(args.warmup):
         lay.run(stream, side)
     torch.cuda.synchronize()
+    step = lambda: lay.run(stream, side)
+    if args.graph:
+        # one step captured as a HIP graph (the side stream forks from and
+        # joins the capture stream inside it; the step allocates nothing and
+        # records no memset) and replayed on a stream of its own
+        graph, main = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+        main.wait_stream(stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=main):
+            lay.run(main, side)
+        torch.cuda.synchronize()
+        stream = main
+
+        def step():
+            with torch.cuda.stream(main):
+                graph.replay()
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
     # an event on the main stream before every step and after the last: a
     # step's combine waits for its side-stream work, and the next step's
     # side-stream work waits for that combine, so consecutive events bracket
@@ -436,7 +459,7 @@ def main():
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     ev[0].record(stream)
     for i in range(args.steps):
-        lay.run(stream, side)
+        step()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
@@ -494,7 +517,7 @@ def main():
                    "experts": sh.n_experts, "top_k": k, "ep_ranks": sh.n_ranks, "local_experts": sh.local_experts,
                    "waves": sh.waves, "expert_hidden": sh.expert_hidden, "shared_experts": sh.shared_experts,
                    "shared_hidden": sh.shared_hidden, "send_cap": scap, "recv_cap": rcap, "gather": args.gather,
-                   "live_waves": lay.live_waves, "streams": args.streams if full else 1,
+                   "live_waves": lay.live_waves, "streams": args.streams if full else 1, "hip_graph": args.graph,
                    "parallelism": "one EP rank of 64 (the other ranks' pools and returns are inputs)"},
     }
     if kind is not None:
