@@ -161,6 +161,46 @@ def test_router_logits_exact_on_the_grid():
             assert Fraction(float(l[t, e])) == exact
 
 
+def test_grid_sums_are_exact_in_fp32_in_any_order():
+    """What lets the GPU's logits be compared bit for bit on the exact grid:
+    at d_model 6144 every partial sum of grid products is an integer multiple
+    of 2^-(s+2) below 2^24 units, so float32 addition in any order (natural,
+    reversed, shuffled, or in 16- and 64-long blocks summed in another order,
+    as a matrix core does) gives the exact value; and grid values are stored
+    in bf16 without rounding."""
+    sh = configs.get(2)  # the router's shape: d_model 6144, 384 experts
+    inp = gen.generate(configs.with_tokens(sh, 4), seed=6, grid=True, with_foreign=False)
+    x = gen.to_f32(inp["x"])
+    w = gen.to_f32(inp["w_router"])
+    s = int(np.round(-np.log2(np.min(np.abs(w[w != 0])))))
+    a = np.rint(x.astype(np.float64) * 4).astype(np.int64)
+    b = np.rint(w.astype(np.float64) * 2.0 ** s).astype(np.int64)
+    # bf16 storage round-trips every grid value (at most 8 significant bits)
+    assert np.array_equal(gen.to_f32(gen._store(x, "bf16")), x) and np.array_equal(gen.to_f32(gen._store(w, "bf16")), w)
+    rng = np.random.default_rng(3)
+    for t in range(2):
+        for e in (0, 191, 383):
+            exact = np.float64(int(np.dot(a[t], b[e]))) / 2.0 ** (s + 2)
+            prod = x[t] * w[e]  # float32 products, exact here
+            orders = [np.arange(prod.size), np.arange(prod.size)[::-1], rng.permutation(prod.size)]
+            for o in orders:
+                acc = np.float32(0)
+                for v in prod[o]:
+                    acc = np.float32(acc + v)
+                assert np.float64(acc) == exact
+            for blk in (16, 64):
+                parts = [np.float32(0)] * (prod.size // blk)
+                for i in range(prod.size // blk):
+                    p = np.float32(0)
+                    for v in prod[i * blk:(i + 1) * blk]:
+                        p = np.float32(p + v)
+                    parts[i] = p
+                acc = np.float32(0)
+                for i in rng.permutation(len(parts)):
+                    acc = np.float32(acc + parts[i])
+                assert np.float64(acc) == exact
+
+
 def test_router_bias_rows():
     x = np.zeros((10, 4), dtype=np.float32)
     w = np.zeros((3, 4), dtype=np.float32)
